@@ -1,0 +1,156 @@
+"""Plain fp64 CPU oracle for the GPT-2 / nanoGPT causal self-attention layer.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package.  It shares no code with the HIP library
+(``gpt_causal_self_amd``) and imports nothing from it.
+
+The arithmetic lives in ``oracle.c`` (double precision, written from the
+definition on page "nanoGPT global flow", section 2.5 (B) CausalSelfAttention
+and page "nanoGPT architecture explained step by step", section 3).  This
+module only marshals numpy arrays into it.  ``brute.py`` holds a second,
+pure-Python rendering of the same definition for tiny shapes.
+
+Weights are taken as [in, out] (``y = x @ W + b``), the transpose of the
+``nn.Linear`` storage.
+
+Parity pins: every function here is pinned by the CPU tests in
+``tests/test_oracle_pins.py`` (brute force, library special cases, closed
+forms, invariants, finite differences, planted-mistake checks).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the C oracle with gcc (portable -O2, no fast-math, so no sum
+    is reassociated).  Returns the path of the shared library."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-pthread", "-Wall",
+           "-fno-fast-math", "-ffp-contract=off", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _declare(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    i = ctypes.c_int
+    lib.oracle_forward.restype = i
+    lib.oracle_forward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
+                                   dp, dp, dp, dp, i]
+    lib.oracle_backward.restype = i
+    lib.oracle_backward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
+                                    dp, dp, dp, dp, dp, dp, dp, i]
+    return lib
+
+
+def load(path: str | None = None):
+    """Load the oracle library (building it first if it is not there)."""
+    global _lib
+    if path is not None:
+        return _declare(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = _declare(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def forward(x, W_attn, b_attn, W_proj, b_proj, n_head, *, want=("y",),
+            nthreads=None, lib=None):
+    """Causal self-attention forward in fp64.
+
+    x [B,T,C]; W_attn [C,3C]; b_attn [3C] or None; W_proj [C,C];
+    b_proj [C] or None.  ``want`` selects outputs among
+    "y" [B,T,C], "qkv" [B,T,3C], "ym" [B,T,C] (merged heads before c_proj),
+    "P" [B,H,T,T] (attention probabilities), "lse" [B,H,T].
+    Returns a dict of float64 arrays."""
+    lib = lib or load()
+    x = _f64(x)
+    B, T, C = x.shape
+    H = int(n_head)
+    W_attn, b_attn, W_proj, b_proj = map(_f64, (W_attn, b_attn, W_proj, b_proj))
+    assert W_attn.shape == (C, 3 * C) and W_proj.shape == (C, C)
+    assert b_attn is None or b_attn.shape == (3 * C,)
+    assert b_proj is None or b_proj.shape == (C,)
+    out = {"y": np.empty((B, T, C))}
+    if "qkv" in want:
+        out["qkv"] = np.empty((B, T, 3 * C))
+    if "ym" in want:
+        out["ym"] = np.empty((B, T, C))
+    if "P" in want:
+        out["P"] = np.empty((B, H, T, T))
+    if "lse" in want:
+        out["lse"] = np.empty((B, H, T))
+    rc = lib.oracle_forward(B, T, C, H, _ptr(x), _ptr(W_attn), _ptr(b_attn),
+                            _ptr(W_proj), _ptr(b_proj), _ptr(out["y"]),
+                            _ptr(out.get("qkv")), _ptr(out.get("ym")),
+                            _ptr(out.get("P")), _ptr(out.get("lse")),
+                            int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_forward failed (bad shape or out of memory)")
+    return {k: v for k, v in out.items() if k in want}
+
+
+def backward(x, W_attn, b_attn, W_proj, b_proj, dY, n_head, *, want_inter=False,
+             nthreads=None, lib=None):
+    """Exact fp64 gradient of the layer for upstream gradient dY [B,T,C].
+
+    Returns dict with dx, dW_attn, dW_proj and (when the layer has biases)
+    db_attn, db_proj; with ``want_inter`` also dqkv [B,T,3C] and dym."""
+    lib = lib or load()
+    x = _f64(x)
+    B, T, C = x.shape
+    H = int(n_head)
+    W_attn, b_attn, W_proj, b_proj, dY = map(_f64, (W_attn, b_attn, W_proj, b_proj, dY))
+    assert dY.shape == x.shape
+    out = {"dx": np.empty((B, T, C)), "dW_attn": np.empty((C, 3 * C)),
+           "dW_proj": np.empty((C, C))}
+    if b_attn is not None:
+        out["db_attn"] = np.empty(3 * C)
+    if b_proj is not None:
+        out["db_proj"] = np.empty(C)
+    if want_inter:
+        out["dqkv"] = np.empty((B, T, 3 * C))
+        out["dym"] = np.empty((B, T, C))
+    rc = lib.oracle_backward(B, T, C, H, _ptr(x), _ptr(W_attn), _ptr(b_attn),
+                             _ptr(W_proj), _ptr(b_proj), _ptr(dY),
+                             _ptr(out["dx"]), _ptr(out["dW_attn"]),
+                             _ptr(out.get("db_attn")), _ptr(out["dW_proj"]),
+                             _ptr(out.get("db_proj")), _ptr(out.get("dqkv")),
+                             _ptr(out.get("dym")),
+                             int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_backward failed (bad shape or out of memory)")
+    return out

@@ -1,0 +1,377 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for the GPT-2 / nanoGPT causal
+ * self-attention layer (forward and exact backward).
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT.  Only the test suite, the
+ * smoke check and the CPU-baseline leg of the benchmark may load this code.
+ * It shares no source, header or build step with the HIP library.
+ *
+ * What it computes, and where each step comes from:
+ *   page "nanoGPT global flow" (devpress.csdn.net), section 2.5 (B)
+ *   CausalSelfAttention, and page "nanoGPT architecture explained step by
+ *   step" (lzwjava.github.io), section 3 (causal self-attention) with its
+ *   closing formula Attention(Q,K,V) = softmax(Q K^T / sqrt(d_k)) V.
+ *
+ *   1. qkv = x . W_attn + b_attn               (c_attn, one fused linear)
+ *   2. q, k, v = column blocks [0,C), [C,2C), [2C,3C) of qkv; head h owns
+ *      columns [h*hs, (h+1)*hs) of each block  (split, view, transpose)
+ *   3. s_ij = (q_i . k_j) * (1/sqrt(hs))       (scores, scale)
+ *   4. s_ij = -inf for j > i, diagonal kept    (tril mask, masked_fill)
+ *   5. p_ij = softmax over j of s_ij           (row softmax)
+ *   6. o_i  = sum_j p_ij v_j                   (att @ v)
+ *   7. y_m[b,i,h*hs+d] = o[b,h,i,d]            (transpose back, merge heads)
+ *   8. y = y_m . W_proj + b_proj               (c_proj)
+ *   Dropout is the identity (dropout 0.0 in GPTConfig, page "nanoGPT global
+ *   flow", section 2.1).
+ *
+ * Weights are taken as [in, out] row-major, i.e. the transpose of the
+ * nn.Linear storage: y = x . W + b.
+ *
+ * The softmax is the two-pass textbook form over the whole visible row
+ * (max, then exponentials, then the sum, then division); future positions
+ * get probability exactly 0, which is what masked_fill(-inf) followed by
+ * softmax produces.
+ *
+ * The backward is the exact gradient of steps 1-8 by the chain rule (the
+ * pages only say that autograd applies the chain rule; page "nanoGPT global
+ * flow", section 3 training loop).  The softmax gradient uses the Jacobian
+ * form dS_ij = p_ij (dP_ij - sum_j' p_ij' dP_ij').
+ *
+ * Everything is double precision; callers pass the exact values the GPU
+ * receives (bf16 and fp32 upcast exactly).  Work is split over threads by
+ * output rows or by (batch, head) pairs only; no sum is reordered.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* A minimal parallel-for: items [0, n) handed out one by one.        */
+/* ------------------------------------------------------------------ */
+typedef void (*item_fn)(void *ctx, long item, double *scratch);
+
+typedef struct {
+  item_fn fn;
+  void *ctx;
+  long n;
+  long next; /* shared counter */
+  size_t scratch_doubles;
+  int failed;
+} pool_t;
+
+static void *pool_worker(void *arg) {
+  pool_t *p = (pool_t *)arg;
+  double *scratch = NULL;
+  if (p->scratch_doubles) {
+    scratch = (double *)malloc(p->scratch_doubles * sizeof(double));
+    if (!scratch) {
+      __atomic_store_n(&p->failed, 1, __ATOMIC_SEQ_CST);
+      return NULL;
+    }
+  }
+  for (;;) {
+    long i = __atomic_fetch_add(&p->next, 1, __ATOMIC_SEQ_CST);
+    if (i >= p->n) break;
+    p->fn(p->ctx, i, scratch);
+  }
+  free(scratch);
+  return NULL;
+}
+
+static int parallel_for(long n, int nthreads, item_fn fn, void *ctx,
+                        size_t scratch_doubles) {
+  pool_t p = {fn, ctx, n, 0, scratch_doubles, 0};
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t tid[256];
+  int started = 0;
+  for (int t = 1; t < nthreads; ++t) {
+    if (pthread_create(&tid[started], NULL, pool_worker, &p) != 0) break;
+    ++started;
+  }
+  pool_worker(&p);
+  for (int t = 0; t < started; ++t) pthread_join(tid[t], NULL);
+  return p.failed ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dense linear layer: out[m][n] = bias[n] + sum_k in[m][k] * W[k][n]  */
+/* (nn.Linear with the weight given as [in, out]).  One item = one row. */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  int K, N;
+  const double *in, *W, *bias;
+  double *out;
+} linear_ctx;
+
+static void linear_row(void *vctx, long m, double *scratch) {
+  (void)scratch;
+  const linear_ctx *c = (const linear_ctx *)vctx;
+  double *row = c->out + (size_t)m * c->N;
+  for (int n = 0; n < c->N; ++n) row[n] = 0.0;
+  for (int k = 0; k < c->K; ++k) {
+    const double a = c->in[(size_t)m * c->K + k];
+    const double *w = c->W + (size_t)k * c->N;
+    for (int n = 0; n < c->N; ++n) row[n] += a * w[n];
+  }
+  if (c->bias)
+    for (int n = 0; n < c->N; ++n) row[n] += c->bias[n];
+}
+
+static int linear(int M, int K, int N, const double *in, const double *W,
+                  const double *bias, double *out, int nthreads) {
+  linear_ctx c = {K, N, in, W, bias, out};
+  return parallel_for(M, nthreads, linear_row, &c, 0);
+}
+
+/* ------------------------------------------------------------------ */
+/* Causal attention for one (b, h) pair.                               */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  int B, T, C, H;
+  const double *qkv; /* [B*T][3C] */
+  double *ym;        /* [B*T][C] merged heads */
+  double *P;         /* optional [B][H][T][T] */
+  double *lse;       /* optional [B][H][T] */
+} attn_ctx;
+
+/* Probabilities of query row i of head (b, h): p[j] for j <= i.
+ * s_j = (q_i . k_j) / sqrt(hs); two-pass softmax.  Returns the row's
+ * log-sum-exp log(sum_j exp(s_j)). */
+static double prob_row(const double *qkv, int T, int C, int H, int b, int h,
+                       int i, double *p) {
+  const int hs = C / H;
+  const size_t ld = (size_t)3 * C;
+  const double scale = 1.0 / sqrt((double)hs);
+  const double *q = qkv + ((size_t)b * T + i) * ld + (size_t)h * hs;
+  double m = -INFINITY;
+  for (int j = 0; j <= i; ++j) {
+    const double *k = qkv + ((size_t)b * T + j) * ld + C + (size_t)h * hs;
+    double dot = 0.0;
+    for (int d = 0; d < hs; ++d) dot += q[d] * k[d];
+    p[j] = dot * scale;
+    if (p[j] > m) m = p[j];
+  }
+  double Z = 0.0;
+  for (int j = 0; j <= i; ++j) {
+    p[j] = exp(p[j] - m);
+    Z += p[j];
+  }
+  for (int j = 0; j <= i; ++j) p[j] /= Z;
+  return m + log(Z);
+}
+
+static void attn_head(void *vctx, long item, double *p) {
+  const attn_ctx *c = (const attn_ctx *)vctx;
+  const int b = (int)(item / c->H), h = (int)(item % c->H);
+  const int T = c->T, C = c->C, H = c->H, hs = C / H;
+  const size_t ld = (size_t)3 * C;
+  for (int i = 0; i < T; ++i) {
+    const double l = prob_row(c->qkv, T, C, H, b, h, i, p);
+    double *o = c->ym + ((size_t)b * T + i) * C + (size_t)h * hs;
+    for (int d = 0; d < hs; ++d) o[d] = 0.0;
+    for (int j = 0; j <= i; ++j) {
+      const double *v =
+          c->qkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;
+      for (int d = 0; d < hs; ++d) o[d] += p[j] * v[d];
+    }
+    if (c->P) {
+      double *row = c->P + (((size_t)b * H + h) * T + i) * T;
+      for (int j = 0; j < T; ++j) row[j] = (j <= i) ? p[j] : 0.0;
+    }
+    if (c->lse) c->lse[((size_t)b * H + h) * T + i] = l;
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Forward.                                                            */
+/* ------------------------------------------------------------------ */
+/* x [B][T][C], W_attn [C][3C], b_attn [3C] or NULL, W_proj [C][C],
+ * b_proj [C] or NULL.  Outputs: y [B][T][C] (required); qkv [B][T][3C],
+ * ym [B][T][C], P [B][H][T][T], lse [B][H][T] (each optional, NULL = not
+ * wanted).  Returns 0, or -1 on bad arguments / allocation failure. */
+int oracle_forward(int B, int T, int C, int H, const double *x,
+                   const double *W_attn, const double *b_attn,
+                   const double *W_proj, const double *b_proj, double *y,
+                   double *qkv_out, double *ym_out, double *P_out,
+                   double *lse_out, int nthreads) {
+  if (B < 0 || T < 0 || C <= 0 || H <= 0 || C % H != 0) return -1;
+  if (!x || !W_attn || !W_proj || !y) return -1;
+  const long M = (long)B * T;
+  if (M == 0) return 0;
+  double *qkv = qkv_out ? qkv_out : (double *)malloc((size_t)M * 3 * C * sizeof(double));
+  double *ym = ym_out ? ym_out : (double *)malloc((size_t)M * C * sizeof(double));
+  int rc = -1;
+  if (!qkv || !ym) goto done;
+  if (linear((int)M, C, 3 * C, x, W_attn, b_attn, qkv, nthreads)) goto done;
+  {
+    attn_ctx a = {B, T, C, H, qkv, ym, P_out, lse_out};
+    if (parallel_for((long)B * H, nthreads, attn_head, &a, (size_t)T)) goto done;
+  }
+  if (linear((int)M, C, C, ym, W_proj, b_proj, y, nthreads)) goto done;
+  rc = 0;
+done:
+  if (!qkv_out) free(qkv);
+  if (!ym_out) free(ym);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Backward pieces.                                                    */
+/* ------------------------------------------------------------------ */
+/* dW[k][n] = sum_m in[m][k] * dout[m][n]; one item = one row k. */
+typedef struct {
+  int M, K, N;
+  const double *in, *dout;
+  double *dW;
+} wgrad_ctx;
+
+static void wgrad_row(void *vctx, long k, double *scratch) {
+  (void)scratch;
+  const wgrad_ctx *c = (const wgrad_ctx *)vctx;
+  double *row = c->dW + (size_t)k * c->N;
+  for (int n = 0; n < c->N; ++n) row[n] = 0.0;
+  for (int m = 0; m < c->M; ++m) {
+    const double a = c->in[(size_t)m * c->K + k];
+    const double *g = c->dout + (size_t)m * c->N;
+    for (int n = 0; n < c->N; ++n) row[n] += a * g[n];
+  }
+}
+
+/* db[n] = sum_m dout[m][n] (single thread; cheap). */
+static void bias_grad(int M, int N, const double *dout, double *db) {
+  for (int n = 0; n < N; ++n) db[n] = 0.0;
+  for (int m = 0; m < M; ++m)
+    for (int n = 0; n < N; ++n) db[n] += dout[(size_t)m * N + n];
+}
+
+/* din[m][k] = sum_n dout[m][n] * W[k][n]; one item = one row m. */
+typedef struct {
+  int K, N;
+  const double *dout, *W;
+  double *din;
+} dgrad_ctx;
+
+static void dgrad_row(void *vctx, long m, double *scratch) {
+  (void)scratch;
+  const dgrad_ctx *c = (const dgrad_ctx *)vctx;
+  const double *g = c->dout + (size_t)m * c->N;
+  for (int k = 0; k < c->K; ++k) {
+    const double *w = c->W + (size_t)k * c->N;
+    double s = 0.0;
+    for (int n = 0; n < c->N; ++n) s += g[n] * w[n];
+    c->din[(size_t)m * c->K + k] = s;
+  }
+}
+
+/* Attention backward for one (b, h): from dym (gradient of the merged
+ * heads) to the q, k, v column blocks of dqkv. */
+typedef struct {
+  int B, T, C, H;
+  const double *qkv, *dym;
+  double *dqkv;
+} attn_bwd_ctx;
+
+static void attn_bwd_head(void *vctx, long item, double *scratch) {
+  const attn_bwd_ctx *c = (const attn_bwd_ctx *)vctx;
+  const int b = (int)(item / c->H), h = (int)(item % c->H);
+  const int T = c->T, C = c->C, H = c->H, hs = C / H;
+  const size_t ld = (size_t)3 * C;
+  const double scale = 1.0 / sqrt((double)hs);
+  double *p = scratch;       /* [T] probabilities of row i */
+  double *dp = scratch + T;  /* [T] dL/dp_ij               */
+  /* zero this head's dq, dk, dv columns */
+  for (int t = 0; t < T; ++t) {
+    double *r = c->dqkv + ((size_t)b * T + t) * ld + (size_t)h * hs;
+    for (int d = 0; d < hs; ++d) r[d] = r[C + d] = r[2 * C + d] = 0.0;
+  }
+  for (int i = 0; i < T; ++i) {
+    prob_row(c->qkv, T, C, H, b, h, i, p);
+    const double *dO = c->dym + ((size_t)b * T + i) * C + (size_t)h * hs;
+    const double *qi = c->qkv + ((size_t)b * T + i) * ld + (size_t)h * hs;
+    /* dp_ij = dO_i . v_j ;  dv_j += p_ij dO_i */
+    double rowdot = 0.0;
+    for (int j = 0; j <= i; ++j) {
+      const double *vj = c->qkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;
+      double *dvj = c->dqkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;
+      double s = 0.0;
+      for (int d = 0; d < hs; ++d) {
+        s += dO[d] * vj[d];
+        dvj[d] += p[j] * dO[d];
+      }
+      dp[j] = s;
+      rowdot += p[j] * s;
+    }
+    /* softmax Jacobian: ds_ij = p_ij (dp_ij - sum_j' p_ij' dp_ij');
+     * scores s_ij = scale q_i . k_j  =>  dq_i += scale ds_ij k_j,
+     * dk_j += scale ds_ij q_i */
+    double *dqi = c->dqkv + ((size_t)b * T + i) * ld + (size_t)h * hs;
+    for (int j = 0; j <= i; ++j) {
+      const double ds = p[j] * (dp[j] - rowdot);
+      const double *kj = c->qkv + ((size_t)b * T + j) * ld + C + (size_t)h * hs;
+      double *dkj = c->dqkv + ((size_t)b * T + j) * ld + C + (size_t)h * hs;
+      for (int d = 0; d < hs; ++d) {
+        dqi[d] += scale * ds * kj[d];
+        dkj[d] += scale * ds * qi[d];
+      }
+    }
+  }
+}
+
+/* Exact gradient of the layer for upstream gradient dY [B][T][C].
+ * Outputs (each required, fully overwritten): dx [B][T][C],
+ * dW_attn [C][3C], dW_proj [C][C]; db_attn [3C] and db_proj [C] are
+ * written when non-NULL (NULL = the layer has no bias).  Optional:
+ * dqkv [B][T][3C] and dym [B][T][C] intermediates. */
+int oracle_backward(int B, int T, int C, int H, const double *x,
+                    const double *W_attn, const double *b_attn,
+                    const double *W_proj, const double *b_proj,
+                    const double *dY, double *dx, double *dW_attn,
+                    double *db_attn, double *dW_proj, double *db_proj,
+                    double *dqkv_out, double *dym_out, int nthreads) {
+  if (B < 0 || T < 0 || C <= 0 || H <= 0 || C % H != 0) return -1;
+  if (!x || !W_attn || !W_proj || !dY || !dx || !dW_attn || !dW_proj) return -1;
+  const long M = (long)B * T;
+  int rc = -1;
+  double *qkv = (double *)malloc(((size_t)M * 3 * C + 1) * sizeof(double));
+  double *ym = (double *)malloc(((size_t)M * C + 1) * sizeof(double));
+  double *y = (double *)malloc(((size_t)M * C + 1) * sizeof(double));
+  double *dym = dym_out ? dym_out : (double *)malloc(((size_t)M * C + 1) * sizeof(double));
+  double *dqkv = dqkv_out ? dqkv_out : (double *)malloc(((size_t)M * 3 * C + 1) * sizeof(double));
+  if (!qkv || !ym || !y || !dym || !dqkv) goto done;
+  if (oracle_forward(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, y, qkv, ym,
+                     NULL, NULL, nthreads))
+    goto done;
+  /* c_proj: y = ym . W_proj + b_proj */
+  if (db_proj) bias_grad((int)M, C, dY, db_proj);
+  {
+    wgrad_ctx w = {(int)M, C, C, ym, dY, dW_proj};
+    if (parallel_for(C, nthreads, wgrad_row, &w, 0)) goto done;
+    dgrad_ctx g = {C, C, dY, W_proj, dym};
+    if (parallel_for(M, nthreads, dgrad_row, &g, 0)) goto done;
+  }
+  /* attention core */
+  {
+    attn_bwd_ctx a = {B, T, C, H, qkv, dym, dqkv};
+    if (parallel_for((long)B * H, nthreads, attn_bwd_head, &a, (size_t)2 * T + 2))
+      goto done;
+  }
+  /* c_attn: qkv = x . W_attn + b_attn */
+  if (db_attn) bias_grad((int)M, 3 * C, dqkv, db_attn);
+  {
+    wgrad_ctx w = {(int)M, C, 3 * C, x, dqkv, dW_attn};
+    if (parallel_for(C, nthreads, wgrad_row, &w, 0)) goto done;
+    dgrad_ctx g = {C, 3 * C, dqkv, W_attn, dx};
+    if (parallel_for(M, nthreads, dgrad_row, &g, 0)) goto done;
+  }
+  (void)b_attn;
+  rc = 0;
+done:
+  free(qkv);
+  free(ym);
+  free(y);
+  if (!dym_out) free(dym);
+  if (!dqkv_out) free(dqkv);
+  return rc;
+}

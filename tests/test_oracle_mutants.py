@@ -1,0 +1,142 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case copies ``oracle/oracle.c``, plants one plausible mistake (a dropped
+term, a wrong sign, a wrong index or offset, a transposed operand, a missing
+scale or normalisation), compiles the copy into a temporary library and runs
+a quick subset of the pins against it: brute-force loops, the T = 1 closed
+form, torch fp64 autograd and finite differences.  Every mutant has to fail at
+least one of them; the unmodified source has to pass all of them.  All of this
+runs on the CPU; the oracle in the tree is never modified.
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.brute as brute
+from gpt_causal_self_amd.inputs import make_inputs
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+# (name, [(old, new, occurrence index or None for every occurrence)])
+MUTANTS = [
+    ("bias dropped", [("row[n] += c->bias[n]", "row[n] += 0.0", 0)]),
+    ("scale without sqrt", [("const double scale = 1.0 / sqrt((double)hs);",
+                             "const double scale = 1.0 / (double)hs;", 0)]),
+    ("future keys visible", [("for (int j = 0; j <= i; ++j)", "for (int j = 0; j < T; ++j)", k)
+                             for k in (0, 0, 0, 0)]),
+    ("diagonal masked", [("for (int j = 0; j <= i; ++j)", "for (int j = 0; j < i; ++j)", k)
+                         for k in (0, 0, 0, 0)]),
+    ("key read from value block",
+     [("const double *k = qkv + ((size_t)b * T + j) * ld + C + (size_t)h * hs;",
+       "const double *k = qkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;", 0)]),
+    ("query head offset dropped",
+     [("const double *q = qkv + ((size_t)b * T + i) * ld + (size_t)h * hs;",
+       "const double *q = qkv + ((size_t)b * T + i) * ld;", 0)]),
+    ("heads merged in reverse order",
+     [("double *o = c->ym + ((size_t)b * T + i) * C + (size_t)h * hs;",
+       "double *o = c->ym + ((size_t)b * T + i) * C + (size_t)(H - 1 - h) * hs;", 0)]),
+    ("softmax not normalised", [("p[j] /= Z;", "p[j] /= 1.0;", 0)]),
+    ("exp argument negated", [("p[j] = exp(p[j] - m);", "p[j] = exp(m - p[j]);", 0)]),
+    ("log-sum-exp loses max", [("return m + log(Z);", "return log(Z);", 0)]),
+    ("square weight transposed",
+     [("row[n] += a * w[n];",
+       "row[n] += a * (c->K == c->N ? c->W[(size_t)n * c->N + k] : w[n]);", 0)]),
+    ("softmax grad without row term",
+     [("const double ds = p[j] * (dp[j] - rowdot);", "const double ds = p[j] * dp[j];", 0)]),
+    ("key grad sign", [("dkj[d] += scale * ds * qi[d];", "dkj[d] -= scale * ds * qi[d];", 0)]),
+    ("value grad wrong operand", [("dvj[d] += p[j] * dO[d];", "dvj[d] += p[j] * qi[d];", 0)]),
+    ("query grad without scale", [("dqi[d] += scale * ds * kj[d];", "dqi[d] += ds * kj[d];", 0)]),
+    ("bias grad drops last row",
+     [("db[n] += dout[(size_t)m * N + n];",
+       "db[n] += (m + 1 < M) ? dout[(size_t)m * N + n] : 0.0;", 0)]),
+    ("weight grad drops first row",
+     [("for (int m = 0; m < c->M; ++m) {", "for (int m = 1; m < c->M; ++m) {", 0)]),
+    ("input grad with untransposed square weight",
+     [("s += g[n] * w[n];",
+       "s += g[n] * (c->K == c->N ? c->W[(size_t)n * c->N + k] : w[n]);", 0)]),
+]
+
+
+def _apply(src, edits):
+    for old, new, occ in edits:
+        parts = src.split(old)
+        assert len(parts) > occ + 1, f"pattern not found: {old!r}"
+        src = old.join(parts[:occ + 1]) + new + old.join(parts[occ + 1:])
+    return src
+
+
+def _pins(lib):
+    """Quick subset of the oracle's pins; returns the names that failed."""
+    failed = []
+    # brute force forward, incl. P and the log-sum-exp
+    for (B, T, C, H, bias) in ((2, 5, 8, 2, True), (2, 6, 16, 4, False)):
+        inp = make_inputs(B, T, C, H, bias=bias, dtype="f32", seed=T, w_std=0.5,
+                          proj_std=0.5, b_attn_std=0.3, b_proj_std=0.3)
+        try:
+            o = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
+                               H, want=("y", "P", "lse", "qkv"), lib=lib)
+        except Exception:
+            failed.append("forward raised")
+            continue
+        yb, Pb = brute.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, H)
+        if not np.allclose(o["y"], yb, rtol=1e-12, atol=1e-13):
+            failed.append("brute y")
+        if not np.allclose(o["P"], Pb, rtol=1e-12, atol=1e-15):
+            failed.append("brute P")
+        qkv, hs = o["qkv"], C // H
+        for b in range(B):
+            for h in range(H):
+                for i in range(T):
+                    s = [float(qkv[b, i, h * hs:(h + 1) * hs] @
+                               qkv[b, j, C + h * hs:C + (h + 1) * hs]) / math.sqrt(hs)
+                         for j in range(i + 1)]
+                    lse = math.log(sum(math.exp(v) for v in s))
+                    if not abs(o["lse"][b, h, i] - lse) <= 1e-12 * max(1, abs(lse)):
+                        failed.append("lse")
+    # backward against torch fp64 autograd
+    import torch
+    import torch.nn.functional as F
+    B, T, C, H = 2, 7, 16, 2
+    hs = C // H
+    inp = make_inputs(B, T, C, H, bias=True, dtype="f32", seed=2, w_std=0.4,
+                      proj_std=0.4, with_dY=True)
+    try:
+        g = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
+                            inp.dY, H, lib=lib)
+    except Exception:
+        failed.append("backward raised")
+        return failed
+    ts = {k: torch.tensor(np.asarray(getattr(inp, k), np.float64), requires_grad=True)
+          for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj")}
+    qkv = F.linear(ts["x"], ts["W_attn"].T, ts["b_attn"])
+    q, k, v = [t.view(B, T, H, hs).transpose(1, 2) for t in qkv.split(C, 2)]
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+    y = F.linear(o.transpose(1, 2).reshape(B, T, C), ts["W_proj"].T, ts["b_proj"])
+    y.backward(torch.from_numpy(inp.dY.astype(np.float64)))
+    for kk, gk in (("x", "dx"), ("W_attn", "dW_attn"), ("b_attn", "db_attn"),
+                   ("W_proj", "dW_proj"), ("b_proj", "db_proj")):
+        if not np.allclose(g[gk], ts[kk].grad.numpy(), rtol=1e-10, atol=1e-12):
+            failed.append("autograd " + gk)
+    return failed
+
+
+def test_unmodified_oracle_passes_quick_pins(tmp_path):
+    out = str(tmp_path / "liboracle_same.so")
+    oracle.build(SRC, out)
+    assert _pins(oracle.load(out)) == []
+
+
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, edits):
+    src = _apply(open(SRC).read(), edits)
+    path = tmp_path / "oracle_mutant.c"
+    path.write_text(src)
+    out = str(tmp_path / "liboracle_mutant.so")
+    oracle.build(str(path), out)
+    failed = _pins(oracle.load(out))
+    assert failed, f"planted mistake '{name}' was not caught by any pin"

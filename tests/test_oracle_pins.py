@@ -1,0 +1,353 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+The oracle (``oracle/``) is the definition of causal self-attention written
+out in fp64.  These CPU tests tie it to things other than itself:
+  * brute force: pure-Python loops (``oracle/brute.py``) on tiny shapes;
+  * library special case: torch CPU fp64 ``F.linear`` + causal
+    ``scaled_dot_product_attention``, and the pages' manual masked-softmax
+    form, plus torch autograd for the backward;
+  * closed forms and invariants: rows of P sum to 1, zero weight on future
+    positions, causality (bitwise), T = 1 reduces to c_proj(v), constant
+    sequences, the uniform-attention prefix mean, prefix permutation, head
+    permutation and batch independence;
+  * finite differences for the backward;
+  * the weight sizes printed on page "nanoGPT architecture explained step by
+    step", parameter-count table (``tests/golden/param_counts.txt``).
+"""
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.brute as brute
+from gpt_causal_self_amd.inputs import WORKLOADS, make_inputs, workload_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def fwd(inp, want=("y",), lib=None):
+    return oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
+                          inp.n_head, want=want, lib=lib)
+
+
+def tiny(B=2, T=7, C=8, H=2, bias=True, seed=0, **kw):
+    kw.setdefault("w_std", 0.5)
+    kw.setdefault("proj_std", 0.5)
+    kw.setdefault("b_attn_std", 0.3)
+    kw.setdefault("b_proj_std", 0.3)
+    return make_inputs(B, T, C, H, bias=bias, dtype="f32", seed=seed, **kw)
+
+
+# ---------------------------------------------------------------- I1 shapes
+def test_param_counts_match_pages():
+    rows = [l.split() for l in open(os.path.join(GOLDEN, "param_counts.txt"))
+            if l.strip() and not l.startswith("#")]
+    w = workload_inputs(2, B=1, T=1)
+    got = {"c_attn": w.W_attn.shape, "c_proj": w.W_proj.shape}
+    for name, r, c, approx in rows:
+        assert got[name] == (int(r), int(c))
+        assert round(int(r) * int(c) / 1e6, 2) == float(approx)
+
+
+def test_output_shapes():
+    inp = tiny(B=3, T=5, C=12, H=3)
+    o = fwd(inp, want=("y", "qkv", "ym", "P", "lse"))
+    assert o["y"].shape == (3, 5, 12)
+    assert o["qkv"].shape == (3, 5, 36)
+    assert o["ym"].shape == (3, 5, 12)
+    assert o["P"].shape == (3, 3, 5, 5)
+    assert o["lse"].shape == (3, 3, 5)
+
+
+# ------------------------------------------------------------ brute force
+@pytest.mark.parametrize("B,T,C,H,bias", [
+    (1, 1, 4, 1, True), (2, 5, 8, 2, True), (2, 9, 16, 4, False),
+    (1, 9, 16, 1, True), (2, 3, 12, 3, True)])
+def test_brute_force(B, T, C, H, bias):
+    inp = tiny(B, T, C, H, bias=bias, seed=B * 100 + T)
+    o = fwd(inp, want=("y", "P", "lse"))
+    yb, Pb = brute.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj,
+                           inp.b_proj, H)
+    np.testing.assert_allclose(o["y"], np.array(yb), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(o["P"], np.array(Pb), rtol=1e-12, atol=1e-15)
+    # log-sum-exp of the scaled, visible scores, straight from the formula
+    q = o_qkv = fwd(inp, want=("qkv",))["qkv"]
+    hs = C // H
+    for b in range(B):
+        for h in range(H):
+            for i in range(T):
+                s = [sum(q[b, i, h * hs + d] * o_qkv[b, j, C + h * hs + d]
+                         for d in range(hs)) / math.sqrt(hs) for j in range(i + 1)]
+                lse = math.log(sum(math.exp(v) for v in s))
+                assert abs(o["lse"][b, h, i] - lse) <= 1e-12 * max(1, abs(lse))
+
+
+# ------------------------------------------------------ library special case
+def _torch_layer(inp, manual=False):
+    import torch
+    import torch.nn.functional as F
+    t = lambda a: None if a is None else torch.from_numpy(np.asarray(a, np.float64))  # noqa
+    x, Wa, ba, Wp, bp = map(t, (inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj))
+    B, T, C = x.shape
+    H = inp.n_head
+    hs = C // H
+    qkv = F.linear(x, Wa.T, ba)
+    q, k, v = qkv.split(C, dim=2)
+    q = q.view(B, T, H, hs).transpose(1, 2)
+    k = k.view(B, T, H, hs).transpose(1, 2)
+    v = v.view(B, T, H, hs).transpose(1, 2)
+    if manual:
+        att = (q @ k.transpose(-2, -1)) * (1.0 / math.sqrt(hs))
+        mask = torch.tril(torch.ones(T, T, dtype=torch.float64)).view(1, 1, T, T)
+        att = att.masked_fill(mask == 0, float("-inf"))
+        att = F.softmax(att, dim=-1)
+        o = att @ v
+    else:
+        o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+    o = o.transpose(1, 2).contiguous().view(B, T, C)
+    return F.linear(o, Wp.T, bp).numpy()
+
+
+@pytest.mark.parametrize("manual", [False, True])
+@pytest.mark.parametrize("B,T,C,H,bias", [(2, 33, 64, 4, True), (1, 1, 32, 1, True),
+                                          (3, 17, 96, 3, False), (1, 64, 128, 2, True)])
+def test_torch_reference(B, T, C, H, bias, manual):
+    inp = make_inputs(B, T, C, H, bias=bias, dtype="f32", seed=7 + T, w_std=0.1,
+                      proj_std=0.1)
+    y = fwd(inp)["y"]
+    yt = _torch_layer(inp, manual=manual)
+    np.testing.assert_allclose(y, yt, rtol=1e-11, atol=1e-13)
+
+
+# ----------------------------------------------------- invariants I2 - I9
+def test_rows_sum_to_one_and_future_is_zero():
+    inp = tiny(B=2, T=12, C=16, H=4, w_std=1.0)
+    P = fwd(inp, want=("P",))["P"]
+    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12)
+    T = P.shape[-1]
+    upper = np.triu(np.ones((T, T), bool), k=1)
+    assert np.all(P[..., upper] == 0.0)
+    assert np.all(P[..., ~upper] > 0.0)      # diagonal and past are visible
+
+
+def test_value_ones_gives_ones():
+    """W_v = 0, b_v = 1 makes every value vector all-ones; with W_proj = I,
+    b_proj = 0 the output equals the row sums of P, i.e. exactly 1."""
+    B, T, C, H = 2, 20, 16, 4
+    inp = tiny(B, T, C, H, w_std=0.7)
+    inp.W_attn[:, 2 * C:] = 0.0
+    inp.b_attn[2 * C:] = 1.0
+    inp.W_proj[:] = np.eye(C, dtype=np.float32)
+    inp.b_proj[:] = 0.0
+    y = fwd(inp)["y"]
+    np.testing.assert_allclose(y, 1.0, rtol=0, atol=1e-13)
+
+
+def test_causality_bitwise():
+    B, T, C, H = 2, 16, 32, 4
+    inp = tiny(B, T, C, H, w_std=0.3)
+    y0 = fwd(inp)["y"]
+    rng = np.random.default_rng(5)
+    for t in (0, 5, T - 2):
+        pert = tiny(B, T, C, H, w_std=0.3)
+        pert.x[:, t + 1:] += rng.standard_normal(pert.x[:, t + 1:].shape).astype(np.float32)
+        y1 = fwd(pert)["y"]
+        assert np.array_equal(y0[:, :t + 1], y1[:, :t + 1])
+        assert not np.allclose(y0[:, t + 1:], y1[:, t + 1:])
+
+
+def test_T1_is_cproj_of_v():
+    B, C, H = 3, 32, 4
+    inp = tiny(B, 1, C, H, w_std=0.3)
+    y = fwd(inp)["y"]
+    x = inp.x.astype(np.float64)[:, 0]
+    v = x @ inp.W_attn[:, 2 * C:].astype(np.float64) + inp.b_attn[2 * C:]
+    expect = v @ inp.W_proj.astype(np.float64) + inp.b_proj
+    np.testing.assert_allclose(y[:, 0], expect, rtol=1e-13, atol=1e-14)
+
+
+def test_constant_sequence():
+    B, T, C, H = 2, 11, 16, 2
+    inp = tiny(B, T, C, H, w_std=0.4)
+    inp.x[:] = inp.x[:, :1]
+    y = fwd(inp)["y"]
+    y1 = fwd(inp.prefix(1))["y"]
+    np.testing.assert_allclose(y, np.broadcast_to(y1, y.shape), rtol=1e-13, atol=1e-14)
+
+
+def test_zero_query_gives_prefix_mean():
+    B, T, C, H = 2, 13, 16, 4
+    inp = tiny(B, T, C, H, w_std=0.4)
+    inp.W_attn[:, :C] = 0.0
+    inp.b_attn[:C] = 0.0
+    o = fwd(inp, want=("ym", "qkv"))
+    v = o["qkv"][:, :, 2 * C:]
+    mean = np.cumsum(v, axis=1) / np.arange(1, T + 1)[None, :, None]
+    np.testing.assert_allclose(o["ym"], mean, rtol=1e-12, atol=1e-14)
+
+
+def test_prefix_permutation():
+    B, T, C, H = 1, 10, 16, 2
+    inp = tiny(B, T, C, H, w_std=0.5)
+    y0 = fwd(inp)["y"]
+    perm = np.random.default_rng(1).permutation(T - 1)
+    inp.x[:, :T - 1] = inp.x[:, perm]
+    y1 = fwd(inp)["y"]
+    np.testing.assert_allclose(y1[:, T - 1], y0[:, T - 1], rtol=1e-12, atol=1e-14)
+
+
+def test_head_permutation_and_batch_independence():
+    B, T, C, H = 3, 9, 24, 3
+    hs = C // H
+    inp = tiny(B, T, C, H, w_std=0.5)
+    y0 = fwd(inp)["y"]
+    perm = [2, 0, 1]
+    cols = np.concatenate([np.arange(p * hs, (p + 1) * hs) for p in perm])
+    allcols = np.concatenate([cols, C + cols, 2 * C + cols])
+    pinp = tiny(B, T, C, H, w_std=0.5)
+    pinp.W_attn[:] = inp.W_attn[:, allcols]
+    pinp.b_attn[:] = inp.b_attn[allcols]
+    pinp.W_proj[:] = inp.W_proj[cols, :]
+    y1 = fwd(pinp)["y"]
+    np.testing.assert_allclose(y1, y0, rtol=1e-12, atol=1e-14)
+    # batch independence: each sample alone gives the same rows, bitwise
+    for b in range(B):
+        yb = fwd(inp.batch(b, b + 1))["y"]
+        assert np.array_equal(yb[0], y0[b])
+
+
+def test_single_head_is_plain_attention():
+    """H = 1: one head of size C; compare with a direct numpy formula."""
+    B, T, C = 2, 8, 8
+    inp = tiny(B, T, C, 1, w_std=0.5)
+    o = fwd(inp, want=("ym", "qkv"))
+    qkv = o["qkv"]
+    for b in range(B):
+        q, k, v = qkv[b, :, :C], qkv[b, :, C:2 * C], qkv[b, :, 2 * C:]
+        s = q @ k.T / math.sqrt(C)
+        s[np.triu(np.ones((T, T), bool), 1)] = -np.inf
+        p = np.exp(s - s.max(1, keepdims=True))
+        p /= p.sum(1, keepdims=True)
+        np.testing.assert_allclose(o["ym"][b], p @ v, rtol=1e-12, atol=1e-14)
+
+
+def test_empty_batch():
+    inp = tiny(B=2, T=4, C=8, H=2)
+    e = inp.batch(0, 0)
+    assert fwd(e)["y"].shape == (0, 4, 8)
+
+
+# ------------------------------------------------------------- backward
+def _loss(inp, lib=None):
+    return float((fwd(inp, lib=lib)["y"] * inp.dY.astype(np.float64)).sum())
+
+
+def _fd_check(inp, n_per_tensor, rng, lib=None, eps=1e-6, tol=1e-6):
+    g = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
+                        inp.dY, inp.n_head, lib=lib)
+    # finite differences need fp64 inputs: work on float64 copies
+    import dataclasses
+    base = dataclasses.replace(
+        inp, **{k: (None if getattr(inp, k) is None else getattr(inp, k).astype(np.float64))
+                for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj", "dY")})
+    worst = 0.0
+    for name, gname in (("x", "dx"), ("W_attn", "dW_attn"), ("b_attn", "db_attn"),
+                        ("W_proj", "dW_proj"), ("b_proj", "db_proj")):
+        a = getattr(base, name)
+        if a is None:
+            continue
+        flat = a.reshape(-1)
+        for idx in rng.choice(flat.size, size=min(n_per_tensor, flat.size), replace=False):
+            old = flat[idx]
+            flat[idx] = old + eps
+            lp = _loss(base, lib)
+            flat[idx] = old - eps
+            lm = _loss(base, lib)
+            flat[idx] = old
+            fd = (lp - lm) / (2 * eps)
+            an = g[gname].reshape(-1)[idx]
+            err = abs(fd - an) / max(1.0, abs(an))
+            worst = max(worst, err)
+            assert err <= tol, (name, idx, fd, an)
+    return worst
+
+
+def test_backward_finite_differences_tiny():
+    inp = make_inputs(2, 6, 8, 2, bias=True, dtype="f32", seed=3, w_std=0.5,
+                      proj_std=0.5, with_dY=True)
+    _fd_check(inp, 40, np.random.default_rng(0))
+
+
+def test_backward_finite_differences_tiny_char_shape():
+    """The tiny char workload's shape (B8 T64 C128 H4), 64 entries per tensor."""
+    inp = workload_inputs(1, with_dY=True)
+    _fd_check(inp, 64, np.random.default_rng(1))
+
+
+def test_backward_matches_torch_autograd():
+    import torch
+    B, T, C, H = 2, 19, 32, 4
+    inp = make_inputs(B, T, C, H, bias=True, dtype="f32", seed=11, w_std=0.2,
+                      proj_std=0.2, with_dY=True)
+    g = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
+                        inp.dY, H)
+    ts = {k: torch.tensor(np.asarray(getattr(inp, k), np.float64), requires_grad=True)
+          for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj")}
+    import torch.nn.functional as F
+    hs = C // H
+    qkv = F.linear(ts["x"], ts["W_attn"].T, ts["b_attn"])
+    q, k, v = [t.view(B, T, H, hs).transpose(1, 2) for t in qkv.split(C, 2)]
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True)
+    y = F.linear(o.transpose(1, 2).reshape(B, T, C), ts["W_proj"].T, ts["b_proj"])
+    y.backward(torch.from_numpy(inp.dY.astype(np.float64)))
+    for k, gk in (("x", "dx"), ("W_attn", "dW_attn"), ("b_attn", "db_attn"),
+                  ("W_proj", "dW_proj"), ("b_proj", "db_proj")):
+        np.testing.assert_allclose(g[gk], ts[k].grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_no_bias():
+    inp = make_inputs(1, 5, 8, 2, bias=False, dtype="f32", seed=4, w_std=0.5,
+                      proj_std=0.5, with_dY=True)
+    g = oracle.backward(inp.x, inp.W_attn, None, inp.W_proj, None, inp.dY, 2)
+    assert "db_attn" not in g and "db_proj" not in g
+    _fd_check(inp, 20, np.random.default_rng(2))
+
+
+def test_backward_causality():
+    """An upstream gradient that is non-zero only at position t reaches the
+    input only at positions <= t (the mask blocks every later position)."""
+    B, T, C, H = 1, 8, 16, 2
+    inp = make_inputs(B, T, C, H, bias=True, dtype="f32", seed=9, w_std=0.5,
+                      proj_std=0.5, with_dY=True)
+    t = 3
+    inp.dY[:, :t] = 0.0
+    inp.dY[:, t + 1:] = 0.0
+    g = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
+                        inp.dY, H)
+    assert np.all(g["dx"][:, t + 1:] == 0.0)
+    assert np.any(g["dx"][:, :t] != 0.0)
+
+
+# ----------------------------------------------------------- workloads
+def test_workload_table():
+    """Shapes of the named workloads and the c_proj init rule
+    std = 0.02 / sqrt(2 * n_layer)."""
+    assert WORKLOADS[2].proj_std == pytest.approx(0.02 / math.sqrt(24))
+    assert WORKLOADS[2].proj_std == pytest.approx(0.0041, abs=5e-5)
+    for i, w in WORKLOADS.items():
+        assert w.C % w.H == 0
+        assert w.hs in (32, 64)
+
+
+def test_workload_prefix_is_causal_cut():
+    """A ragged cut of the gpt2-xl-shape workload is a prefix of the full
+    draw, so its output must be the prefix of the full output (bitwise)."""
+    full = workload_inputs(4, B=1, T=40)
+    cut = full.prefix(17)
+    yf = fwd(full)["y"]
+    yc = fwd(cut)["y"]
+    assert np.array_equal(yf[:, :17], yc)
