@@ -1,0 +1,248 @@
+"""Benchmark of the causal self-attention layer on one MI355X.
+
+A step is one forward of the whole layer (c_attn GEMM -> fused causal
+attention -> c_proj GEMM) over one batch of the GPT-2 124M attention layer
+workload: B=12, T=1024, C=768, 12 heads, bf16 with fp32 accumulation, seeded
+synthetic inputs (x ~ N(0,1), weights at the GPT-2 initialisation).  The
+inputs of 8 rotating sets (x, weights, y: 8 x 42.5 MB, larger than the 256 MB
+Infinity Cache) are resident in HBM before timing starts.
+
+Reported (one JSON line): layer TFLOP/s with the causal FLOP count
+F = 8*B*T*C^2 + 2*B*T*(T+1)*C, tokens/s, fraction of the 2.5166 PFLOP/s dense
+bf16 MFMA peak, per-kernel times from HIP events recorded by the library on
+the launch stream, the roofline of the dominant kernel, the training step
+(forward + backward) time of the same workload, and the CPU oracle timed on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+METRIC = ("attention-layer TFLOP/s + tokens/s at B=12,T=1024,C=768,H=12 bf16; "
+          "% of MFMA peak")
+N_SETS = 8
+
+
+def layer_flops(B, T, C):
+    """Causal algorithmic FLOPs of one forward: the two projections
+    (2*B*T*C*3C + 2*B*T*C*C) plus QK^T and PV over the B*T*(T+1)/2 visible
+    (query, key) pairs per head (2*hs FLOPs each, twice, summed over heads)."""
+    return 8 * B * T * C * C + 2 * B * T * (T + 1) * C
+
+
+def stage_flops(B, T, C):
+    return {"c_attn": 6 * B * T * C * C, "attention": 2 * B * T * (T + 1) * C,
+            "c_proj": 2 * B * T * C * C}
+
+
+def stage_bytes(B, T, C, H, es=2, lse=False):
+    """Algorithmic HBM bytes per launch: every tensor read or written once."""
+    BT = B * T
+    return {"c_attn": (BT * C + 3 * C * C + 3 * C + 3 * BT * C) * es,
+            "attention": (3 * BT * C + BT * C) * es + (B * H * T * 4 if lse else 0),
+            "c_proj": (BT * C + C * C + C + BT * C) * es}
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (timing on the library's
+    launch stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a),
+                                          ctypes.c_void_p(b))
+        assert rc == 0, rc
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(workload_index, n_seq):
+    """The fp64 oracle, as it stands, on the first n_seq sequences of the
+    same workload (sequences are independent, so throughput scales)."""
+    import oracle
+    from gpt_causal_self_amd.inputs import workload_inputs
+    inp = workload_inputs(workload_index, B=n_seq)
+    threads = oracle.default_threads()
+    oracle.load()
+    t0 = time.perf_counter()
+    oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.n_head,
+                   nthreads=threads)
+    dt = time.perf_counter() - t0
+    B, T, C = inp.x.shape
+    return {"value": layer_flops(B, T, C) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "tokens_per_s": B * T / dt, "seconds": dt,
+            "sample": f"{n_seq} of 12 sequences (B={n_seq}, T=1024, C=768, H=12), "
+                      "fp64 forward, same seeded inputs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-train", action="store_true", help="skip the fwd+bwd measurement")
+    ap.add_argument("--cpu-seqs", type=int, default=12)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer runs on a single device; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gpt_causal_self_amd import gpt_attn as ga
+    from gpt_causal_self_amd.inputs import WORKLOADS, make_inputs, to_torch
+
+    w = WORKLOADS[2]
+    B, T, C, H = w.B, w.T, w.C, w.H
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sets = []
+    for s in range(N_SETS):
+        inp = make_inputs(B, T, C, H, bias=True, dtype="bf16", seed=125 + 1000 * s,
+                          w_std=w.w_std, b_attn_std=w.b_attn_std, proj_std=w.proj_std,
+                          b_proj_std=w.b_proj_std, with_dY=(s == 0))
+        t = {k: to_torch(getattr(inp, k), "bf16", dev)
+             for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj")}
+        t["y"] = torch.empty_like(t["x"])
+        if s == 0:
+            t["dY"] = to_torch(inp.dY, "bf16", dev)
+        sets.append(t)
+    layer = ga.Layer(C, H, B, T, "bf16")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        t = sets[i % N_SETS]
+        ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"], t["W_proj"],
+                            t["b_proj"], H, t["y"], stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps; the library records 4 events per step on the
+    # launch stream (before c_attn, after c_attn, after attention, after c_proj)
+    ev = HipEvents()
+    events = [ev.create(4) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ga.gpt_attn_set_stage_events(layer.h, events[i])
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ga.gpt_attn_set_stage_events(layer.h, None)
+
+    per = {"c_attn": [], "attention": [], "c_proj": [], "layer": []}
+    for e in events:
+        per["c_attn"].append(ev.elapsed_ms(e[0], e[1]))
+        per["attention"].append(ev.elapsed_ms(e[1], e[2]))
+        per["c_proj"].append(ev.elapsed_ms(e[2], e[3]))
+        per["layer"].append(ev.elapsed_ms(e[0], e[3]))
+    for e in events:
+        ev.destroy(e)
+    mean = {k: sum(v) / len(v) for k, v in per.items()}
+    ms_per_step = wall * 1e3 / args.steps
+
+    F = layer_flops(B, T, C)
+    tflops = F / (ms_per_step * 1e-3) / 1e12
+    sf = stage_flops(B, T, C)
+    sb = stage_bytes(B, T, C, H)
+    kernels = {}
+    for k in ("c_attn", "attention", "c_proj"):
+        kernels[k] = {"ms": round(mean[k], 5),
+                      "tflops": round(sf[k] / (mean[k] * 1e-3) / 1e12, 2),
+                      "gbs": round(sb[k] / (mean[k] * 1e-3) / 1e9, 1),
+                      "flop_per_launch": sf[k], "bytes_per_launch": sb[k]}
+    dom = max(("c_attn", "attention", "c_proj"), key=lambda k: mean[k])
+    achieved = sf[dom] / (mean[dom] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+    out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": "gpt2-124M causal self-attention layer forward, "
+                                  "B=12 T=1024 C=768 H=12 hs=64 bias bf16/fp32-acc",
+                      "B": B, "T": T, "C": C, "n_head": H, "bias": True, "global_batch": B,
+                      "seq_len": T, "parallelism": "single GPU"},
+           "tokens_per_s": round(B * T / (ms_per_step * 1e-3), 1),
+           "frac_of_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+           "flop_per_step": F, "flop_count": "causal: 8BTC^2 + 2BT(T+1)C",
+           "dense_convention_tflops": round((8 * B * T * C * C + 4 * B * T * T * C)
+                                            / (ms_per_step * 1e-3) / 1e12, 2),
+           "event_layer_ms": round(mean["layer"], 5),
+           "kernels": kernels, "roofline": roofline}
+
+    if not args.no_train:
+        try:
+            t = sets[0]
+            g = {"dx": torch.empty_like(t["x"]), "dWa": torch.empty_like(t["W_attn"]),
+                 "dba": torch.empty_like(t["b_attn"]), "dWp": torch.empty_like(t["W_proj"]),
+                 "dbp": torch.empty_like(t["b_proj"])}
+
+            def train_step():
+                ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"], t["W_proj"],
+                                    t["b_proj"], H, t["y"], stream=stream,
+                                    save_for_backward=True)
+                ga.gpt_attn_backward(layer.h, t["x"], t["W_attn"], t["W_proj"], t["dY"],
+                                     g["dx"], g["dWa"], g["dba"], g["dWp"], g["dbp"],
+                                     stream=stream)
+            for _ in range(5):
+                train_step()
+            torch.cuda.synchronize()
+            n = max(10, args.steps // 4)
+            t0 = time.perf_counter()
+            for _ in range(n):
+                train_step()
+            torch.cuda.synchronize()
+            tms = (time.perf_counter() - t0) * 1e3 / n
+            out["train_step"] = {"workload": "gpt2-124M fwd+bwd B=12 T=1024 C=768 H=12 bf16",
+                                 "ms": round(tms, 5),
+                                 "tflops": round(3 * F / (tms * 1e-3) / 1e12, 2),
+                                 "flop_count": "3 x forward causal count"}
+        except ga.GptAttnError as e:
+            out["train_step"] = {"error": str(e)}
+
+    if not args.no_cpu:
+        cb = cpu_baseline(2, args.cpu_seqs)
+        out["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v)
+                               for k, v in cb.items()}
+    layer.close()
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,295 @@
+// attn_fwd.cuh -- fused causal attention forward for gfx950.
+//
+// Computes, for every (batch b, head h, query i):
+//   o_i = sum_{j <= i} softmax_j(q_i . k_j / sqrt(hs)) v_j
+// (page "nanoGPT global flow walkthrough", section 2.5 (B), forward steps 3-6:
+// scores scaled by 1/sqrt(hs), tril mask to -inf, row softmax, att @ v) and
+// writes o straight into the merged-head layout y_m[b][i][h*hs + d] (step 7's
+// transpose + view), never materialising the T x T score matrix.
+//
+// bf16 kernel (MFMA).  One block = 4 waves = 128 queries of one (b, h); each
+// wave owns 32 queries.  Keys and values are streamed through LDS in tiles of
+// 64 (two LDS buffers; the next tile's global loads are issued before the
+// current tile's math).  Per tile a wave computes S^T = K Q^T (keys on the
+// MFMA rows, its 32 queries on the columns) with 32x32x16 bf16 MFMAs, so each
+// lane holds 32 scores of ONE query: the row max / row sum of the online
+// softmax are a local reduction plus one exchange with the other lane half.
+// The probabilities, rounded to bf16, are already laid out as the B operand
+// of O^T += V^T P^T; the V^T operand is read from a transposed LDS copy of the
+// value tile with the matching key order.  Softmax statistics are fp32 in the
+// exp2 domain (scale * log2(e) folded into one multiply).  Tiles entirely above
+// the diagonal are never loaded; a wave skips a tile that lies entirely in
+// its future; diagonal tiles are masked in place.  Heavier (later) query
+// tiles are dispatched first.
+//
+// fp32 kernel (FMA).  One wave of 64 threads per 64 queries, one query per
+// thread, key/value tiles in LDS, online softmax key by key.
+#pragma once
+
+#include "common.cuh"
+
+namespace gpt_attn {
+
+constexpr int kAttnBQ = 128;  // queries per block (bf16 kernel)
+constexpr int kAttnBK = 64;   // keys per tile
+
+template <int HS>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kg,
+    const bf16_t* __restrict__ Vg, bf16_t* __restrict__ O, float* __restrict__ lse,
+    int H, int T, float scale_log2) {
+  static_assert(HS == 32 || HS == 64, "head size");
+  constexpr int KP = HS + 8;        // K tile pitch (elements)
+  constexpr int VP = kAttnBK + 4;   // V^T tile pitch (elements)
+  constexpr int KCH = kAttnBK * HS / 8;          // 16-byte chunks per K tile
+  constexpr int KPER = (KCH + 255) / 256;
+  constexpr int VBLK = (kAttnBK / 4) * (HS / 4);  // 4 keys x 4 dims blocks
+  __shared__ __align__(16) bf16_t Ks[2][kAttnBK * KP];
+  __shared__ __align__(16) bf16_t Vt[2][HS * VP];
+
+  const int nqt = (T + kAttnBQ - 1) / kAttnBQ;
+  const int bh = blockIdx.x;
+  const int qt = nqt - 1 - (int)blockIdx.y;  // heavy tiles first
+  const int H_ = H;
+  const int b = bh / H_, h = bh - b * H_;
+  const size_t head = (size_t)bh * T * HS;
+  const bf16_t* Qh = Q + head;
+  const bf16_t* Kh = Kg + head;
+  const bf16_t* Vh = Vg + head;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int hi = lane >> 5;                 // lane half
+  const int q0 = qt * kAttnBQ + wid * 32;   // first query of this wave
+  const int myq = q0 + (lane & 31);
+
+  // Q^T fragments: lane holds q[myq][16*kk + 8*hi + 0..7]
+  bf16x8 qf[HS / 16];
+#pragma unroll
+  for (int kk = 0; kk < HS / 16; ++kk) {
+    if (myq < T)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)myq * HS + 16 * kk + 8 * hi);
+    else
+      qf[kk] = bf16x8{};
+  }
+
+  floatx16 acc[HS / 32];
+#pragma unroll
+  for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int kv_end = min(T, (qt + 1) * kAttnBQ);
+  const int nkv = (kv_end + kAttnBK - 1) / kAttnBK;
+
+  // register staging of one K/V tile
+  uint4 kr[KPER];
+  uint2 vr[4];
+  auto gload = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int c = tid + i * 256;
+      const int key = c / (HS / 8), dc = c % (HS / 8);
+      if (c < KCH && j0 + key < T)
+        kr[i] = *reinterpret_cast<const uint4*>(Kh + (size_t)(j0 + key) * HS + dc * 8);
+      else
+        kr[i] = make_uint4(0, 0, 0, 0);
+    }
+    const int dg = tid % (HS / 4), kg = tid / (HS / 4);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int key = j0 + kg * 4 + kk;
+      if (tid < VBLK && key < T)
+        vr[kk] = *reinterpret_cast<const uint2*>(Vh + (size_t)key * HS + dg * 4);
+      else
+        vr[kk] = make_uint2(0, 0);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < KPER; ++i) {
+      const int c = tid + i * 256;
+      const int key = c / (HS / 8), dc = c % (HS / 8);
+      if (c < KCH) *reinterpret_cast<uint4*>(&Ks[buf][key * KP + dc * 8]) = kr[i];
+    }
+    if (tid < VBLK) {
+      const int dg = tid % (HS / 4), kg = tid / (HS / 4);
+      // transpose 4 keys x 4 dims -> 4 dims x 4 keys
+#pragma unroll
+      for (int dd = 0; dd < 4; ++dd) {
+        const int sh = (dd & 1) * 16;
+        const uint32_t e0 = ((dd < 2 ? vr[0].x : vr[0].y) >> sh) & 0xffffu;
+        const uint32_t e1 = ((dd < 2 ? vr[1].x : vr[1].y) >> sh) & 0xffffu;
+        const uint32_t e2 = ((dd < 2 ? vr[2].x : vr[2].y) >> sh) & 0xffffu;
+        const uint32_t e3 = ((dd < 2 ? vr[3].x : vr[3].y) >> sh) & 0xffffu;
+        uint2 o;
+        o.x = e0 | (e1 << 16);
+        o.y = e2 | (e3 << 16);
+        *reinterpret_cast<uint2*>(&Vt[buf][(dg * 4 + dd) * VP + kg * 4]) = o;
+      }
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int it = 0; it < nkv; ++it) {
+    const int buf = it & 1;
+    const int j0 = it * kAttnBK;
+    if (it + 1 < nkv) gload(j0 + kAttnBK);
+
+    if (j0 <= q0 + 31) {  // some key of the tile is visible to this wave
+      // ---- S^T = K Q^T for keys j0 .. j0+63 (two 32-key halves)
+      floatx16 s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < HS / 16; ++kk) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+              &Ks[buf][(kt * 32 + (lane & 31)) * KP + 16 * kk + 8 * hi]);
+          s[kt] = mfma32(kf, qf[kk], s[kt]);
+        }
+      }
+      // ---- scale, causal mask, tile max
+      const bool diag = (j0 + kAttnBK - 1 > q0);
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float t = s[kt][r] * scale_log2;
+          if (diag) {
+            const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (key > myq) t = -INFINITY;
+          }
+          s[kt][r] = t;
+          tmax = fmaxf(tmax, t);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float m_new = fmaxf(m, tmax);  // finite: key 0 was seen first
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[kt][r] - m_new);
+          s[kt][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32);
+      l = l * alpha + rs;
+      m = m_new;
+#pragma unroll
+      for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+
+      // ---- O^T += V^T P^T.  P^T operand: lane holds, for key group (kt, u),
+      // keys kt*32 + 16u + 8*(e/4) + 4*hi + e%4 of its query (e = 0..7).
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          bf16x8 pf;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[kt][8 * u + e];
+          const int kb = kt * 32 + 16 * u + 4 * hi;
+#pragma unroll
+          for (int dt = 0; dt < HS / 32; ++dt) {
+            const bf16_t* vrow = &Vt[buf][(dt * 32 + (lane & 31)) * VP + kb];
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 hi8 = *reinterpret_cast<const uint2*>(vrow + 8);
+            uint4 w;
+            w.x = lo.x; w.y = lo.y; w.z = hi8.x; w.w = hi8.y;
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+            acc[dt] = mfma32(vf, pf, acc[dt]);
+          }
+        }
+    }
+
+    if (it + 1 < nkv) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and write o into the merged-head layout
+  if (myq < T) {
+    const float inv = 1.f / l;
+    const int C = HS * H_;
+    bf16_t* orow = O + ((size_t)b * T + myq) * C + h * HS;
+#pragma unroll
+    for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * hi;
+        uint2 w;
+        w.x = pack_bf16x2(acc[dt][4 * g + 0] * inv, acc[dt][4 * g + 1] * inv);
+        w.y = pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d0) = w;
+      }
+    if (lse != nullptr && hi == 0)
+      lse[(size_t)bh * T + myq] = (m + __log2f(l)) * 0.69314718055994530942f;
+  }
+}
+
+// ---------------------------------------------------------------- fp32
+template <int HS>
+__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ Kg, const float* __restrict__ Vg,
+    float* __restrict__ O, float* __restrict__ lse, int H, int T, float scale_log2) {
+  constexpr int BQ = 64, BKV = 64;
+  __shared__ float Ks[BKV][HS];
+  __shared__ float Vs[BKV][HS];
+  const int bh = blockIdx.x;
+  const int nqt = (T + BQ - 1) / BQ;
+  const int qt = nqt - 1 - (int)blockIdx.y;
+  const int b = bh / H, h = bh - b * H;
+  const size_t head = (size_t)bh * T * HS;
+  const int tid = threadIdx.x;
+  const int myq = qt * BQ + tid;
+  float q[HS], o[HS];
+#pragma unroll
+  for (int d = 0; d < HS; ++d) {
+    q[d] = (myq < T) ? Q[head + (size_t)myq * HS + d] : 0.f;
+    o[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kv_end = min(T, (qt + 1) * BQ);
+  for (int j0 = 0; j0 < kv_end; j0 += BKV) {
+    __syncthreads();
+    for (int e = tid; e < BKV * HS; e += 64) {
+      const int key = e / HS, d = e % HS;
+      const bool ok = j0 + key < T;
+      Ks[key][d] = ok ? Kg[head + (size_t)(j0 + key) * HS + d] : 0.f;
+      Vs[key][d] = ok ? Vg[head + (size_t)(j0 + key) * HS + d] : 0.f;
+    }
+    __syncthreads();
+    const int jmax = min(BKV, min(kv_end, myq + 1) - j0);  // keys j0 .. j0+jmax-1 visible
+    for (int jj = 0; jj < jmax; ++jj) {
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < HS; ++d) dot = fmaf(q[d], Ks[jj][d], dot);
+      const float t = dot * scale_log2;
+      const float m_new = fmaxf(m, t);
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      const float p = __builtin_amdgcn_exp2f(t - m_new);
+      l = l * alpha + p;
+#pragma unroll
+      for (int d = 0; d < HS; ++d) o[d] = fmaf(p, Vs[jj][d], o[d] * alpha);
+      m = m_new;
+    }
+  }
+  if (myq < T) {
+    const int C = HS * H;
+    const float inv = 1.f / l;
+    float* orow = O + ((size_t)b * T + myq) * C + h * HS;
+#pragma unroll
+    for (int d = 0; d < HS; ++d) orow[d] = o[d] * inv;
+    if (lse != nullptr) lse[(size_t)bh * T + myq] = (m + __log2f(l)) * 0.69314718055994530942f;
+  }
+}
+
+}  // namespace gpt_attn

@@ -1,0 +1,453 @@
+// gpt_attn.hip -- C ABI of the causal self-attention layer (include/gpt_attn.h).
+//
+// Host side: argument validation (always before any device call), workspace
+// ownership, and the launch sequence on the caller's stream:
+//   forward : c_attn GEMM (bias + head-major q/k/v scatter)
+//             -> fused causal attention (merged-head output, optional LSE)
+//             -> c_proj GEMM (bias)
+//   backward: see attn_bwd.cuh / the launch sequence in gpt_attn_backward.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <math.h>
+
+#include "../../include/gpt_attn.h"
+#include "attn_bwd.cuh"
+#include "attn_fwd.cuh"
+#include "gemm.cuh"
+
+using namespace gpt_attn;
+
+struct gpt_attn_handle {
+  int C, H, hs, max_B, max_T, dtype;
+  int device;
+  size_t esize;  // bytes per element
+  char* ws;      // one allocation, carved below
+  size_t ws_bytes;
+  // carved regions
+  void* qkv;     // [3][B][H][T][hs]
+  void* o;       // [B][T][C]
+  float* lse;    // [B][H][T]
+  void* dym;     // [B][T][C]     backward: gradient of merged heads
+  void* dqkv;    // [B][T][3C]    backward: gradient of c_attn output
+  float* delta;  // [B][H][T]     backward: rowsum(dO * O)
+  float* part;   // split-K partial sums of weight gradients (fp32)
+  size_t part_elems;
+  // state of the last forward
+  int saved, saved_B, saved_T;
+  // optional stage events (measurement hook)
+  hipEvent_t ev[8];
+  int n_ev;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Upper bound on the split-K slices of the weight-gradient GEMMs, and the
+// number of row slices of the bias-gradient column sums.
+constexpr int kWgradSplits = 8;
+constexpr int kColsumSplits = 64;
+
+int check_dims(int C, int n_head, int max_B, int max_T, int dtype) {
+  if (C <= 0 || n_head <= 0 || max_B <= 0 || max_T <= 0) return GPT_ATTN_ERR_INVALID_ARG;
+  if (dtype != GPT_ATTN_F32 && dtype != GPT_ATTN_BF16) return GPT_ATTN_ERR_INVALID_ARG;
+  if (C % n_head != 0) return GPT_ATTN_ERR_SHAPE;
+  const int hs = C / n_head;
+  if (hs != 32 && hs != 64) return GPT_ATTN_ERR_UNSUPPORTED;
+  // every index below fits in 32 bits per tensor row count / 64-bit offsets
+  if ((long long)max_B * max_T > (1LL << 30)) return GPT_ATTN_ERR_SHAPE;
+  return GPT_ATTN_OK;
+}
+
+struct Layout {
+  size_t qkv, o, lse, dym, dqkv, delta, part, total, part_elems;
+};
+
+Layout layout(int C, int H, int max_B, int max_T, size_t es) {
+  Layout L;
+  const size_t BT = (size_t)max_B * max_T;
+  size_t off = 0;
+  L.qkv = off;   off = align_up(off + 3 * BT * C * es);
+  L.o = off;     off = align_up(off + BT * C * es);
+  L.lse = off;   off = align_up(off + (size_t)max_B * H * max_T * sizeof(float));
+  L.dym = off;   off = align_up(off + BT * C * es);
+  L.dqkv = off;  off = align_up(off + 3 * BT * C * es);
+  L.delta = off; off = align_up(off + (size_t)max_B * H * max_T * sizeof(float));
+  L.part_elems = (size_t)kWgradSplits * C * 3 * C + (size_t)kColsumSplits * 3 * C;
+  L.part = off;  off = align_up(off + L.part_elems * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline void mark(const gpt_attn_handle* h, int i, hipStream_t st) {
+  if (i < h->n_ev) (void)hipEventRecord(h->ev[i], st);
+}
+
+inline int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? GPT_ATTN_OK : GPT_ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gpt_attn_strerror(int code) {
+  switch (code) {
+    case GPT_ATTN_OK: return "ok";
+    case GPT_ATTN_ERR_INVALID_ARG: return "invalid argument (NULL pointer, non-positive size or unknown dtype)";
+    case GPT_ATTN_ERR_SHAPE: return "shape error (C % n_head != 0, n_head mismatch, or B/T above the handle's maximum)";
+    case GPT_ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head size must be 32 or 64)";
+    case GPT_ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case GPT_ATTN_ERR_OOM: return "device workspace allocation failed";
+    case GPT_ATTN_ERR_HIP: return "HIP runtime or kernel launch error";
+    case GPT_ATTN_ERR_STATE: return "backward needs a preceding forward with save_for_backward and the same B, T";
+    default: return "unknown status code";
+  }
+}
+
+int gpt_attn_workspace_bytes(int C, int n_head, int max_B, int max_T, int dtype,
+                             size_t* bytes) {
+  if (!bytes) return GPT_ATTN_ERR_INVALID_ARG;
+  const int rc = check_dims(C, n_head, max_B, max_T, dtype);
+  if (rc) return rc;
+  *bytes = layout(C, n_head, max_B, max_T, dtype == GPT_ATTN_F32 ? 4 : 2).total;
+  return GPT_ATTN_OK;
+}
+
+int gpt_attn_create(gpt_attn_t* out, int C, int n_head, int max_B, int max_T, int dtype) {
+  if (!out) return GPT_ATTN_ERR_INVALID_ARG;
+  *out = nullptr;
+  const int rc = check_dims(C, n_head, max_B, max_T, dtype);
+  if (rc) return rc;
+  gpt_attn_handle* h = (gpt_attn_handle*)calloc(1, sizeof(gpt_attn_handle));
+  if (!h) return GPT_ATTN_ERR_OOM;
+  h->C = C;
+  h->H = n_head;
+  h->hs = C / n_head;
+  h->max_B = max_B;
+  h->max_T = max_T;
+  h->dtype = dtype;
+  h->esize = dtype == GPT_ATTN_F32 ? 4 : 2;
+  const Layout L = layout(C, n_head, max_B, max_T, h->esize);
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    free(h);
+    return GPT_ATTN_ERR_HIP;
+  }
+  void* ws = nullptr;
+  const hipError_t e = hipMalloc(&ws, L.total);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    free(h);
+    return e == hipErrorOutOfMemory ? GPT_ATTN_ERR_OOM : GPT_ATTN_ERR_HIP;
+  }
+  h->ws = (char*)ws;
+  h->ws_bytes = L.total;
+  h->qkv = h->ws + L.qkv;
+  h->o = h->ws + L.o;
+  h->lse = (float*)(h->ws + L.lse);
+  h->dym = h->ws + L.dym;
+  h->dqkv = h->ws + L.dqkv;
+  h->delta = (float*)(h->ws + L.delta);
+  h->part = (float*)(h->ws + L.part);
+  h->part_elems = L.part_elems;
+  *out = h;
+  return GPT_ATTN_OK;
+}
+
+int gpt_attn_destroy(gpt_attn_t h) {
+  if (!h) return GPT_ATTN_OK;
+  int rc = GPT_ATTN_OK;
+  if (h->ws) {
+    if (hipDeviceSynchronize() != hipSuccess) rc = GPT_ATTN_ERR_HIP;
+    if (hipFree(h->ws) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
+  }
+  free(h);
+  return rc;
+}
+
+int gpt_attn_debug_backward(gpt_attn_t h, const void** dym, const void** dqkv,
+                            const void** delta) {
+  if (!h) return GPT_ATTN_ERR_INVALID_ARG;
+  if (dym) *dym = h->dym;
+  if (dqkv) *dqkv = h->dqkv;
+  if (delta) *delta = h->delta;
+  return GPT_ATTN_OK;
+}
+
+int gpt_attn_set_stage_events(gpt_attn_t h, void* const* events, int n) {
+  if (!h) return GPT_ATTN_ERR_INVALID_ARG;
+  if (!events) {
+    h->n_ev = 0;
+    return GPT_ATTN_OK;
+  }
+  if (n < 4) return GPT_ATTN_ERR_INVALID_ARG;
+  h->n_ev = n < 8 ? 4 : 8;
+  for (int i = 0; i < h->n_ev; ++i) h->ev[i] = (hipEvent_t)events[i];
+  return GPT_ATTN_OK;
+}
+
+int gpt_attn_debug_workspace(gpt_attn_t h, const void** qkv, const void** o,
+                             const void** lse) {
+  if (!h) return GPT_ATTN_ERR_INVALID_ARG;
+  if (qkv) *qkv = h->qkv;
+  if (o) *o = h->o;
+  if (lse) *lse = h->lse;
+  return GPT_ATTN_OK;
+}
+
+int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_attn,
+                     const void* b_attn, const void* W_proj, const void* b_proj,
+                     int n_head, void* y, void* stream, int save_for_backward) {
+  // ---- validation (host only)
+  if (!h || !x || !W_attn || !W_proj || !y) return GPT_ATTN_ERR_INVALID_ARG;
+  if (B < 0 || T < 0) return GPT_ATTN_ERR_INVALID_ARG;
+  if (n_head != h->H || B > h->max_B || T > h->max_T) return GPT_ATTN_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(W_attn) || !aligned16(W_proj) || !aligned16(y) ||
+      (b_attn && !aligned16(b_attn)) || (b_proj && !aligned16(b_proj)))
+    return GPT_ATTN_ERR_ALIGN;
+  h->saved = 0;
+  if (B == 0 || T == 0) {  // nothing to compute; an empty backward may follow
+    if (save_for_backward) {
+      h->saved = 1;
+      h->saved_B = B;
+      h->saved_T = T;
+    }
+    return GPT_ATTN_OK;
+  }
+
+  const int C = h->C, H = h->H, hs = h->hs;
+  const int M = B * T;
+  const hipStream_t st = as_stream(stream);
+  const size_t head_elems = (size_t)B * H * T * hs;  // one of q, k, v
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hs));
+  float* lse = save_for_backward ? h->lse : nullptr;
+
+  if (h->dtype == GPT_ATTN_BF16) {
+    const bf16_t* xb = (const bf16_t*)x;
+    bf16_t* qkv = (bf16_t*)h->qkv;
+    bf16_t* o = (bf16_t*)h->o;
+    EpiQKV<bf16_t> e1{qkv, (const bf16_t*)b_attn, B, T, C, H, hs};
+    mark(h, 0, st);
+    launch_gemm_bf16<128, 128, true, false>(xb, C, (const bf16_t*)W_attn, 3 * C, M, 3 * C, C,
+                                            e1, st);
+    mark(h, 1, st);
+    const dim3 agrid(B * H, (T + kAttnBQ - 1) / kAttnBQ);
+    if (hs == 64)
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, agrid, dim3(256), 0, st, qkv,
+                         qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
+    else
+      hipLaunchKernelGGL(attn_fwd_bf16_kernel<32>, agrid, dim3(256), 0, st, qkv,
+                         qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
+    mark(h, 2, st);
+    EpiRowMajor<bf16_t> e3{(bf16_t*)y, C, (const bf16_t*)b_proj};
+    launch_gemm_bf16<128, 128, true, false>(o, C, (const bf16_t*)W_proj, C, M, C, C, e3, st);
+    mark(h, 3, st);
+  } else {
+    const float* xf = (const float*)x;
+    float* qkv = (float*)h->qkv;
+    float* o = (float*)h->o;
+    EpiQKV<float> e1{qkv, (const float*)b_attn, B, T, C, H, hs};
+    mark(h, 0, st);
+    launch_gemm_f32<true, false>(xf, C, (const float*)W_attn, 3 * C, M, 3 * C, C, e1, st);
+    mark(h, 1, st);
+    const dim3 agrid(B * H, (T + 63) / 64);
+    if (hs == 64)
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, agrid, dim3(64), 0, st, qkv,
+                         qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
+    else
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, agrid, dim3(64), 0, st, qkv,
+                         qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
+    mark(h, 2, st);
+    EpiRowMajor<float> e3{(float*)y, C, (const float*)b_proj};
+    launch_gemm_f32<true, false>(o, C, (const float*)W_proj, C, M, C, C, e3, st);
+    mark(h, 3, st);
+  }
+  const int rc = launch_status();
+  if (rc == GPT_ATTN_OK && save_for_backward) {
+    h->saved = 1;
+    h->saved_B = B;
+    h->saved_T = T;
+  }
+  return rc;
+}
+
+int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const void* W_proj,
+                      const void* dY, void* dx, void* dW_attn, void* db_attn, void* dW_proj,
+                      void* db_proj, int B, int T, void* stream) {
+  // ---- validation (host only)
+  if (!h || !x || !W_attn || !W_proj || !dY || !dx || !dW_attn || !dW_proj)
+    return GPT_ATTN_ERR_INVALID_ARG;
+  if (B < 0 || T < 0) return GPT_ATTN_ERR_INVALID_ARG;
+  if (B > h->max_B || T > h->max_T) return GPT_ATTN_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(W_attn) || !aligned16(W_proj) || !aligned16(dY) ||
+      !aligned16(dx) || !aligned16(dW_attn) || !aligned16(dW_proj) ||
+      (db_attn && !aligned16(db_attn)) || (db_proj && !aligned16(db_proj)))
+    return GPT_ATTN_ERR_ALIGN;
+  if (!h->saved || h->saved_B != B || h->saved_T != T) return GPT_ATTN_ERR_STATE;
+
+  const int C = h->C, H = h->H, hs = h->hs;
+  const int M = B * T, N3 = 3 * C;
+  const hipStream_t st = as_stream(stream);
+  const float scale = (float)(1.0 / sqrt((double)hs));
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hs));
+  const size_t head_elems = (size_t)B * H * T * hs;
+  float* part = h->part;                                   // split-K partials
+  float* cpart = h->part + (size_t)kWgradSplits * C * N3;  // column-sum partials
+  const int rows_per = (M + kColsumSplits - 1) / kColsumSplits;
+  const int ncs = rows_per > 0 ? (M + rows_per - 1) / rows_per : 0;
+  auto splits_for = [](int tiles) {
+    int s = (2 * 256 + tiles - 1) / tiles;
+    return s < 1 ? 1 : (s > kWgradSplits ? kWgradSplits : s);
+  };
+  const int rblocks = 1024;
+
+  if (M == 0) {  // empty batch: the weight and bias gradients are zero sums
+    const size_t nwa = (size_t)C * N3, nwp = (size_t)C * C;
+    if (h->dtype == GPT_ATTN_BF16) {
+      hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(rblocks), dim3(256), 0, st, part,
+                         0, nwa, nwa, (bf16_t*)dW_attn);
+      hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(rblocks), dim3(256), 0, st, part,
+                         0, nwp, nwp, (bf16_t*)dW_proj);
+      if (db_attn)
+        hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(16), dim3(256), 0, st, part, 0,
+                           (size_t)N3, (size_t)N3, (bf16_t*)db_attn);
+      if (db_proj)
+        hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(16), dim3(256), 0, st, part, 0,
+                           (size_t)C, (size_t)C, (bf16_t*)db_proj);
+    } else {
+      hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3(rblocks), dim3(256), 0, st, part, 0,
+                         nwa, nwa, (float*)dW_attn);
+      hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3(rblocks), dim3(256), 0, st, part, 0,
+                         nwp, nwp, (float*)dW_proj);
+      if (db_attn)
+        hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3(16), dim3(256), 0, st, part, 0,
+                           (size_t)N3, (size_t)N3, (float*)db_attn);
+      if (db_proj)
+        hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3(16), dim3(256), 0, st, part, 0,
+                           (size_t)C, (size_t)C, (float*)db_proj);
+    }
+    return launch_status();
+  }
+
+  mark(h, 4, st);
+  if (h->dtype == GPT_ATTN_BF16) {
+    const bf16_t* qkv = (const bf16_t*)h->qkv;
+    const bf16_t* o = (const bf16_t*)h->o;
+    bf16_t* dym = (bf16_t*)h->dym;
+    bf16_t* dqkv = (bf16_t*)h->dqkv;
+    // ---- c_proj: dym = dY W_proj^T ; dW_proj = ym^T dY ; db_proj = colsum(dY)
+    EpiRowMajor<bf16_t> e_dym{dym, C, nullptr};
+    launch_gemm_bf16<128, 128, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M, C,
+                                           C, e_dym, st);
+    EpiPartial e_wp{part, C, (size_t)C * C};
+    const int s1 = splits_for(((C + 127) / 128) * ((C + 127) / 128));
+    const int n1 = launch_gemm_bf16<128, 128, false, false>(o, C, (const bf16_t*)dY, C, C, C, M,
+                                                            e_wp, st, s1);
+    hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(rblocks), dim3(256), 0, st, part, n1,
+                       (size_t)C * C, (size_t)C * C, (bf16_t*)dW_proj);
+    if (db_proj) {
+      hipLaunchKernelGGL(colsum_partial_kernel<bf16_t>, dim3((C + 255) / 256, ncs), dim3(256), 0,
+                         st, (const bf16_t*)dY, M, C, C, rows_per, cpart);
+      hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3((C + 255) / 256), dim3(256), 0, st,
+                         cpart, ncs, (size_t)C, (size_t)C, (bf16_t*)db_proj);
+    }
+    mark(h, 5, st);
+    // ---- attention core
+    const dim3 dgrid((unsigned)((M * (long)H + 255) / 256));
+    const dim3 kgrid(B * H, (T + kBwdBK - 1) / kBwdBK);
+    const dim3 qgrid(B * H, (T + 127) / 128);
+    const bf16_t* q = qkv;
+    const bf16_t* k = qkv + head_elems;
+    const bf16_t* v = qkv + 2 * head_elems;
+    if (hs == 64) {
+      hipLaunchKernelGGL((attn_delta_kernel<64, bf16_t>), dgrid, dim3(256), 0, st, dym, o,
+                         h->delta, B, H, T);
+      hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, kgrid, dim3(256), 0, st, q, k, v, dym,
+                         h->lse, h->delta, dqkv, H, T, scale, scale_log2);
+      hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<64>, qgrid, dim3(256), 0, st, q, k, v, dym,
+                         h->lse, h->delta, dqkv, H, T, scale, scale_log2);
+    } else {
+      hipLaunchKernelGGL((attn_delta_kernel<32, bf16_t>), dgrid, dim3(256), 0, st, dym, o,
+                         h->delta, B, H, T);
+      hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<32>, kgrid, dim3(256), 0, st, q, k, v, dym,
+                         h->lse, h->delta, dqkv, H, T, scale, scale_log2);
+      hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<32>, qgrid, dim3(256), 0, st, q, k, v, dym,
+                         h->lse, h->delta, dqkv, H, T, scale, scale_log2);
+    }
+    mark(h, 6, st);
+    // ---- c_attn: dx = dqkv W_attn^T ; dW_attn = x^T dqkv ; db_attn = colsum(dqkv)
+    EpiRowMajor<bf16_t> e_dx{(bf16_t*)dx, C, nullptr};
+    launch_gemm_bf16<128, 128, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3, e_dx,
+                                           st);
+    EpiPartial e_wa{part, N3, (size_t)C * N3};
+    const int s2 = splits_for(((C + 127) / 128) * ((N3 + 127) / 128));
+    const int n2 = launch_gemm_bf16<128, 128, false, false>((const bf16_t*)x, C, dqkv, N3, C, N3,
+                                                            M, e_wa, st, s2);
+    hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(rblocks), dim3(256), 0, st, part, n2,
+                       (size_t)C * N3, (size_t)C * N3, (bf16_t*)dW_attn);
+    if (db_attn) {
+      hipLaunchKernelGGL(colsum_partial_kernel<bf16_t>, dim3((N3 + 255) / 256, ncs), dim3(256), 0,
+                         st, dqkv, M, N3, N3, rows_per, cpart);
+      hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3((N3 + 255) / 256), dim3(256), 0,
+                         st, cpart, ncs, (size_t)N3, (size_t)N3, (bf16_t*)db_attn);
+    }
+  } else {
+    const float* qkv = (const float*)h->qkv;
+    const float* o = (const float*)h->o;
+    float* dym = (float*)h->dym;
+    float* dqkv = (float*)h->dqkv;
+    EpiRowMajor<float> e_dym{dym, C, nullptr};
+    launch_gemm_f32<true, true>((const float*)dY, C, (const float*)W_proj, C, M, C, C, e_dym, st);
+    EpiRowMajor<float> e_wp{(float*)dW_proj, C, nullptr};
+    launch_gemm_f32<false, false>(o, C, (const float*)dY, C, C, C, M, e_wp, st);
+    if (db_proj) {
+      hipLaunchKernelGGL(colsum_partial_kernel<float>, dim3((C + 255) / 256, ncs), dim3(256), 0,
+                         st, (const float*)dY, M, C, C, rows_per, cpart);
+      hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3((C + 255) / 256), dim3(256), 0, st,
+                         cpart, ncs, (size_t)C, (size_t)C, (float*)db_proj);
+    }
+    mark(h, 5, st);
+    const dim3 dgrid((unsigned)((M * (long)H + 255) / 256));
+    const dim3 tgrid((unsigned)((M * (long)H + 63) / 64));
+    const float* q = qkv;
+    const float* k = qkv + head_elems;
+    const float* v = qkv + 2 * head_elems;
+    if (hs == 64) {
+      hipLaunchKernelGGL((attn_delta_kernel<64, float>), dgrid, dim3(256), 0, st, dym, o,
+                         h->delta, B, H, T);
+      hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<64>, tgrid, dim3(64), 0, st, q, k, v, dym,
+                         h->lse, h->delta, dqkv, B, H, T, scale, scale_log2);
+      hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<64>, tgrid, dim3(64), 0, st, q, k, v, dym,
+                         h->lse, h->delta, dqkv, B, H, T, scale, scale_log2);
+    } else {
+      hipLaunchKernelGGL((attn_delta_kernel<32, float>), dgrid, dim3(256), 0, st, dym, o,
+                         h->delta, B, H, T);
+      hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<32>, tgrid, dim3(64), 0, st, q, k, v, dym,
+                         h->lse, h->delta, dqkv, B, H, T, scale, scale_log2);
+      hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<32>, tgrid, dim3(64), 0, st, q, k, v, dym,
+                         h->lse, h->delta, dqkv, B, H, T, scale, scale_log2);
+    }
+    mark(h, 6, st);
+    EpiRowMajor<float> e_dx{(float*)dx, C, nullptr};
+    launch_gemm_f32<true, true>(dqkv, N3, (const float*)W_attn, N3, M, C, N3, e_dx, st);
+    EpiRowMajor<float> e_wa{(float*)dW_attn, N3, nullptr};
+    launch_gemm_f32<false, false>((const float*)x, C, dqkv, N3, C, N3, M, e_wa, st);
+    if (db_attn) {
+      hipLaunchKernelGGL(colsum_partial_kernel<float>, dim3((N3 + 255) / 256, ncs), dim3(256), 0,
+                         st, dqkv, M, N3, N3, rows_per, cpart);
+      hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3((N3 + 255) / 256), dim3(256), 0, st,
+                         cpart, ncs, (size_t)N3, (size_t)N3, (float*)db_attn);
+    }
+  }
+  mark(h, 7, st);
+  return launch_status();
+}
+
+}  // extern "C"

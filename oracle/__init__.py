@@ -49,10 +49,10 @@ def _declare(lib):
     i = ctypes.c_int
     lib.oracle_forward.restype = i
     lib.oracle_forward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
-                                   dp, dp, dp, dp, i]
+                                   dp, dp, dp, dp, i, i]
     lib.oracle_backward.restype = i
     lib.oracle_backward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
-                                    dp, dp, dp, dp, dp, dp, dp, i]
+                                    dp, dp, dp, dp, dp, dp, dp, i, i]
     return lib
 
 
@@ -88,14 +88,16 @@ def _ptr(a):
 
 
 def forward(x, W_attn, b_attn, W_proj, b_proj, n_head, *, want=("y",),
-            nthreads=None, lib=None):
+            store_bf16=(), nthreads=None, lib=None):
     """Causal self-attention forward in fp64.
 
     x [B,T,C]; W_attn [C,3C]; b_attn [3C] or None; W_proj [C,C];
     b_proj [C] or None.  ``want`` selects outputs among
     "y" [B,T,C], "qkv" [B,T,3C], "ym" [B,T,C] (merged heads before c_proj),
     "P" [B,H,T,T] (attention probabilities), "lse" [B,H,T].
-    Returns a dict of float64 arrays."""
+    ``store_bf16`` may name "qkv" and/or "ym": those intermediates are then
+    rounded to bfloat16 (nearest-even) where a bf16 path stores them; all
+    arithmetic stays fp64.  Returns a dict of float64 arrays."""
     lib = lib or load()
     x = _f64(x)
     B, T, C = x.shape
@@ -117,18 +119,25 @@ def forward(x, W_attn, b_attn, W_proj, b_proj, n_head, *, want=("y",),
                             _ptr(W_proj), _ptr(b_proj), _ptr(out["y"]),
                             _ptr(out.get("qkv")), _ptr(out.get("ym")),
                             _ptr(out.get("P")), _ptr(out.get("lse")),
+                            (1 if "qkv" in store_bf16 else 0) | (2 if "ym" in store_bf16 else 0),
                             int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_forward failed (bad shape or out of memory)")
     return {k: v for k, v in out.items() if k in want}
 
 
+_STORE_BITS = {"qkv": 1, "ym": 2, "dym": 4, "dqkv": 8}
+
+
 def backward(x, W_attn, b_attn, W_proj, b_proj, dY, n_head, *, want_inter=False,
-             nthreads=None, lib=None):
+             store_bf16=(), nthreads=None, lib=None):
     """Exact fp64 gradient of the layer for upstream gradient dY [B,T,C].
 
     Returns dict with dx, dW_attn, dW_proj and (when the layer has biases)
-    db_attn, db_proj; with ``want_inter`` also dqkv [B,T,3C] and dym."""
+    db_attn, db_proj; with ``want_inter`` also dqkv [B,T,3C] and dym.
+    ``store_bf16`` may name "qkv", "ym", "dym", "dqkv": those stored tensors
+    are rounded to bfloat16 and the gradients are the exact chain rule
+    through the rounded values."""
     lib = lib or load()
     x = _f64(x)
     B, T, C = x.shape
@@ -150,6 +159,7 @@ def backward(x, W_attn, b_attn, W_proj, b_proj, dY, n_head, *, want_inter=False,
                              _ptr(out.get("db_attn")), _ptr(out["dW_proj"]),
                              _ptr(out.get("db_proj")), _ptr(out.get("dqkv")),
                              _ptr(out.get("dym")),
+                             sum(_STORE_BITS[k] for k in set(store_bf16)),
                              int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_backward failed (bad shape or out of memory)")

@@ -46,6 +46,22 @@
 #include <stdlib.h>
 #include <string.h>
 
+/* Round to the nearest bfloat16 value (8 significant bits), ties to even.
+ * Only used to mimic a path that STORES an intermediate in bfloat16 (the
+ * bf16 path keeps q, k, v and the merged heads in bf16); all arithmetic stays
+ * double.  Normal range only (the layer's values are far from bf16's
+ * limits). */
+static double round_bf16(double v) {
+  if (v == 0.0 || !isfinite(v)) return v;
+  int e;
+  const double f = frexp(v, &e); /* v = f * 2^e, 0.5 <= |f| < 1 */
+  return ldexp(nearbyint(ldexp(f, 8)), e - 8);
+}
+
+static void round_all(double *a, size_t n) {
+  for (size_t i = 0; i < n; ++i) a[i] = round_bf16(a[i]);
+}
+
 /* ------------------------------------------------------------------ */
 /* A minimal parallel-for: items [0, n) handed out one by one.        */
 /* ------------------------------------------------------------------ */
@@ -190,12 +206,14 @@ static void attn_head(void *vctx, long item, double *p) {
 /* x [B][T][C], W_attn [C][3C], b_attn [3C] or NULL, W_proj [C][C],
  * b_proj [C] or NULL.  Outputs: y [B][T][C] (required); qkv [B][T][3C],
  * ym [B][T][C], P [B][H][T][T], lse [B][H][T] (each optional, NULL = not
- * wanted).  Returns 0, or -1 on bad arguments / allocation failure. */
+ * wanted).  store_bf16: bit 0 rounds qkv to bfloat16 after step 1, bit 1
+ * rounds the merged heads after step 7 (0 = exact fp64 throughout).
+ * Returns 0, or -1 on bad arguments / allocation failure. */
 int oracle_forward(int B, int T, int C, int H, const double *x,
                    const double *W_attn, const double *b_attn,
                    const double *W_proj, const double *b_proj, double *y,
                    double *qkv_out, double *ym_out, double *P_out,
-                   double *lse_out, int nthreads) {
+                   double *lse_out, int store_bf16, int nthreads) {
   if (B < 0 || T < 0 || C <= 0 || H <= 0 || C % H != 0) return -1;
   if (!x || !W_attn || !W_proj || !y) return -1;
   const long M = (long)B * T;
@@ -205,10 +223,12 @@ int oracle_forward(int B, int T, int C, int H, const double *x,
   int rc = -1;
   if (!qkv || !ym) goto done;
   if (linear((int)M, C, 3 * C, x, W_attn, b_attn, qkv, nthreads)) goto done;
+  if (store_bf16 & 1) round_all(qkv, (size_t)M * 3 * C);
   {
     attn_ctx a = {B, T, C, H, qkv, ym, P_out, lse_out};
     if (parallel_for((long)B * H, nthreads, attn_head, &a, (size_t)T)) goto done;
   }
+  if (store_bf16 & 2) round_all(ym, (size_t)M * C);
   if (linear((int)M, C, C, ym, W_proj, b_proj, y, nthreads)) goto done;
   rc = 0;
 done:
@@ -323,13 +343,18 @@ static void attn_bwd_head(void *vctx, long item, double *scratch) {
  * Outputs (each required, fully overwritten): dx [B][T][C],
  * dW_attn [C][3C], dW_proj [C][C]; db_attn [3C] and db_proj [C] are
  * written when non-NULL (NULL = the layer has no bias).  Optional:
- * dqkv [B][T][3C] and dym [B][T][C] intermediates. */
+ * dqkv [B][T][3C] and dym [B][T][C] intermediates.
+ * store_bf16 rounds stored tensors to bfloat16 where a bf16 path stores
+ * them: bit 0 qkv and bit 1 the merged heads (as in oracle_forward), bit 2
+ * the gradient of the merged heads, bit 3 the gradient of qkv; every
+ * gradient is then the exact chain rule through those stored values. */
 int oracle_backward(int B, int T, int C, int H, const double *x,
                     const double *W_attn, const double *b_attn,
                     const double *W_proj, const double *b_proj,
                     const double *dY, double *dx, double *dW_attn,
                     double *db_attn, double *dW_proj, double *db_proj,
-                    double *dqkv_out, double *dym_out, int nthreads) {
+                    double *dqkv_out, double *dym_out, int store_bf16,
+                    int nthreads) {
   if (B < 0 || T < 0 || C <= 0 || H <= 0 || C % H != 0) return -1;
   if (!x || !W_attn || !W_proj || !dY || !dx || !dW_attn || !dW_proj) return -1;
   const long M = (long)B * T;
@@ -341,7 +366,7 @@ int oracle_backward(int B, int T, int C, int H, const double *x,
   double *dqkv = dqkv_out ? dqkv_out : (double *)malloc(((size_t)M * 3 * C + 1) * sizeof(double));
   if (!qkv || !ym || !y || !dym || !dqkv) goto done;
   if (oracle_forward(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, y, qkv, ym,
-                     NULL, NULL, nthreads))
+                     NULL, NULL, store_bf16 & 3, nthreads))
     goto done;
   /* c_proj: y = ym . W_proj + b_proj */
   if (db_proj) bias_grad((int)M, C, dY, db_proj);
@@ -351,12 +376,14 @@ int oracle_backward(int B, int T, int C, int H, const double *x,
     dgrad_ctx g = {C, C, dY, W_proj, dym};
     if (parallel_for(M, nthreads, dgrad_row, &g, 0)) goto done;
   }
+  if (store_bf16 & 4) round_all(dym, (size_t)M * C);
   /* attention core */
   {
     attn_bwd_ctx a = {B, T, C, H, qkv, dym, dqkv};
     if (parallel_for((long)B * H, nthreads, attn_bwd_head, &a, (size_t)2 * T + 2))
       goto done;
   }
+  if (store_bf16 & 8) round_all(dqkv, (size_t)M * 3 * C);
   /* c_attn: qkv = x . W_attn + b_attn */
   if (db_attn) bias_grad((int)M, 3 * C, dqkv, db_attn);
   {

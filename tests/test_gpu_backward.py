@@ -1,0 +1,142 @@
+"""GPU parity of the backward path (training step) against the fp64 oracle.
+
+The oracle's gradients are the exact chain rule through the layer (pinned on
+the CPU by finite differences and torch autograd).  The GPU returns them in
+the parameter dtype with fp32 accumulation.  fp32 results are held to a
+maximum absolute error of 1e-4; bf16 results to the gradient gate derived in
+``grad_gate.py`` (the stated bf16 tolerance widened by six standard
+deviations of the bf16 rounding noise of each contraction) plus a normwise
+gate of 1e-2."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpt_causal_self_amd import gpt_attn as ga
+from gpt_causal_self_amd.inputs import from_torch, make_inputs, workload_inputs
+import grad_gate
+from layer_helpers import device_inputs
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dx", "dW_attn", "db_attn", "dW_proj", "db_proj")
+
+
+def gpu_train_step(inp, layer=None):
+    import torch
+    B, T, C = inp.x.shape
+    own = layer is None
+    if own:
+        layer = ga.Layer(C, inp.n_head, max(B, 1), max(T, 1), inp.dtype)
+    t = device_inputs(inp)
+    y = layer.forward(t["x"], t["W_attn"], t["b_attn"], t["W_proj"], t["b_proj"],
+                      save_for_backward=True)
+    g = layer.backward(t["x"], t["W_attn"], t["W_proj"], t["dY"],
+                       has_bias=inp.b_attn is not None)
+    torch.cuda.synchronize()
+    out = {k: from_torch(v) for k, v in g.items()}
+    out["y"] = from_torch(y)
+    if own:
+        layer.close()
+    return out
+
+
+def check_grads(inp):
+    g = gpu_train_step(inp)
+    r = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY,
+                        inp.n_head, want_inter=True)
+    if inp.dtype == "bf16":
+        r["ym"] = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
+                                 inp.n_head, want=("ym",))["ym"]
+        sig = grad_gate.sigmas(inp, r)
+    errs = {}
+    for k in GRADS:
+        if k not in r:
+            assert k not in g
+            continue
+        if inp.dtype == "f32":
+            err = np.abs(g[k] - r[k]).max()
+            assert err <= 1e-4, (k, err)
+            errs[k] = err
+        else:
+            errs[k] = grad_gate.check(k, g[k], r[k], sig[k])
+    return errs
+
+
+def test_backward_tiny_char_fp32():
+    check_grads(workload_inputs(1, with_dY=True))
+
+
+@pytest.mark.parametrize("B,T,C,H,bias,dtype", [
+    (2, 300, 768, 12, True, "bf16"),
+    (3, 200, 256, 8, True, "bf16"),      # hs 32
+    (1, 131, 1600, 25, False, "bf16"),   # odd head count, no bias
+    (2, 77, 320, 5, True, "f32"),
+    (3, 1, 128, 2, True, "bf16"),        # T = 1
+    (1, 2, 64, 2, True, "bf16"),
+    (2, 129, 768, 12, True, "bf16"),     # one key past a 128-key tile
+])
+def test_backward_small_shapes(B, T, C, H, bias, dtype):
+    inp = make_inputs(B, T, C, H, bias=bias, dtype=dtype, seed=7 * B + T, with_dY=True)
+    check_grads(inp)
+
+
+def test_backward_training_step_workload_full():
+    """The GPT-2 124M training step at its full shape (B12 T1024 C768 H12):
+    every gradient against the full fp64 oracle backward."""
+    check_grads(workload_inputs(5))
+
+
+def test_backward_deterministic():
+    inp = make_inputs(2, 200, 768, 12, dtype="bf16", seed=31, with_dY=True)
+    a = gpu_train_step(inp)
+    b = gpu_train_step(inp)
+    for k in GRADS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_state_errors():
+    import torch
+    inp = make_inputs(2, 40, 128, 2, dtype="bf16", seed=3, with_dY=True)
+    t = device_inputs(inp)
+    layer = ga.Layer(128, 2, 2, 64, "bf16")
+    gr = {k: torch.empty_like(v) for k, v in (("dx", t["x"]), ("dWa", t["W_attn"]),
+                                               ("dWp", t["W_proj"]))}
+    args = (t["x"], t["W_attn"], t["W_proj"], t["dY"], gr["dx"], gr["dWa"], None,
+            gr["dWp"], None)
+    # forward without save -> STATE
+    layer.forward(t["x"], t["W_attn"], t["b_attn"], t["W_proj"], t["b_proj"])
+    with pytest.raises(ga.GptAttnError) as e:
+        ga.gpt_attn_backward(layer.h, *args)
+    assert e.value.code == ga.ERR_STATE
+    # saved with T = 40, backward asks for T = 20 -> STATE
+    layer.forward(t["x"], t["W_attn"], t["b_attn"], t["W_proj"], t["b_proj"],
+                  save_for_backward=True)
+    with pytest.raises(ga.GptAttnError) as e:
+        ga.gpt_attn_backward(layer.h, *args, B=2, T=20)
+    assert e.value.code == ga.ERR_STATE
+    ga.gpt_attn_backward(layer.h, *args)        # matching shapes: fine
+    torch.cuda.synchronize()
+    layer.close()
+
+
+def test_backward_empty_batch_gives_zero_weight_grads():
+    import torch
+    inp = make_inputs(1, 8, 128, 2, dtype="bf16", seed=4, with_dY=True)
+    t = device_inputs(inp)
+    layer = ga.Layer(128, 2, 1, 8, "bf16")
+    y = torch.empty_like(t["x"])
+    ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"], t["W_proj"], t["b_proj"], 2,
+                        y, save_for_backward=True, B=0, T=8)
+    dWa = torch.full_like(t["W_attn"], 3.0)
+    dWp = torch.full_like(t["W_proj"], 3.0)
+    dba = torch.full_like(t["b_attn"], 3.0)
+    dbp = torch.full_like(t["b_proj"], 3.0)
+    dx = torch.empty_like(t["x"])
+    ga.gpt_attn_backward(layer.h, t["x"], t["W_attn"], t["W_proj"], t["dY"], dx, dWa, dba, dWp,
+                         dbp, B=0, T=8)
+    torch.cuda.synchronize()
+    for v in (dWa, dWp, dba, dbp):
+        assert torch.all(v == 0)
+    layer.close()

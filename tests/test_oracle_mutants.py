@@ -56,6 +56,10 @@ MUTANTS = [
        "db[n] += (m + 1 < M) ? dout[(size_t)m * N + n] : 0.0;", 0)]),
     ("weight grad drops first row",
      [("for (int m = 0; m < c->M; ++m) {", "for (int m = 1; m < c->M; ++m) {", 0)]),
+    ("bf16 rounding keeps 7 bits", [("ldexp(nearbyint(ldexp(f, 8)), e - 8)",
+                                     "ldexp(nearbyint(ldexp(f, 7)), e - 7)", 0)]),
+    ("bf16 rounding truncates", [("ldexp(nearbyint(ldexp(f, 8)), e - 8)",
+                                  "ldexp(trunc(ldexp(f, 8)), e - 8)", 0)]),
     ("input grad with untransposed square weight",
      [("s += g[n] * w[n];",
        "s += g[n] * (c->K == c->N ? c->W[(size_t)n * c->N + k] : w[n]);", 0)]),
@@ -73,6 +77,15 @@ def _apply(src, edits):
 def _pins(lib):
     """Quick subset of the oracle's pins; returns the names that failed."""
     failed = []
+    # bf16 storage rounding against integer rounding of the fp64 bit pattern
+    from test_oracle_pins import _bits_rne_bf16
+    inp = make_inputs(2, 5, 16, 2, dtype="f32", seed=4, w_std=0.3, proj_std=0.3)
+    ex = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, 2,
+                        want=("qkv",), lib=lib)["qkv"]
+    rq = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, 2,
+                        want=("qkv",), store_bf16=("qkv",), lib=lib)["qkv"]
+    if not np.array_equal(rq, _bits_rne_bf16(ex)):
+        failed.append("bf16 rounding")
     # brute force forward, incl. P and the log-sum-exp
     for (B, T, C, H, bias) in ((2, 5, 8, 2, True), (2, 6, 16, 4, False)):
         inp = make_inputs(B, T, C, H, bias=bias, dtype="f32", seed=T, w_std=0.5,

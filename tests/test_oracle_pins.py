@@ -351,3 +351,79 @@ def test_workload_prefix_is_causal_cut():
     yf = fwd(full)["y"]
     yc = fwd(cut)["y"]
     assert np.array_equal(yf[:, :17], yc)
+
+
+# ------------------------------------------------- bf16 storage emulation
+def _bits_rne_bf16(a):
+    """Round float64 values to bfloat16 (8 significant bits, nearest even)
+    by integer arithmetic on the fp64 bit pattern: keep the top 7 explicit
+    mantissa bits, i.e. drop the low 45 bits with round-half-even."""
+    u = np.ascontiguousarray(a, np.float64).view(np.uint64)
+    drop = np.uint64(45)
+    half = np.uint64(1 << 44)
+    lsb = (u >> drop) & np.uint64(1)
+    r = ((u + half - np.uint64(1) + lsb) >> drop) << drop
+    return r.view(np.float64)
+
+
+def test_store_bf16_rounds_to_nearest_even():
+    inp = make_inputs(2, 9, 32, 2, dtype="f32", seed=21, w_std=0.3, proj_std=0.3)
+    exact = fwd(inp, want=("qkv", "ym"))
+    r = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, 2,
+                       want=("qkv", "ym"), store_bf16=("qkv",))
+    assert np.array_equal(r["qkv"], _bits_rne_bf16(exact["qkv"]))
+    assert not np.array_equal(r["qkv"], exact["qkv"])
+    r2 = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, 2,
+                        want=("ym",), store_bf16=("ym",))
+    assert np.array_equal(r2["ym"], _bits_rne_bf16(exact["ym"]))
+    # tie cases: exactly half-way values go to the even neighbour
+    ties = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, -(1 + 2.0 ** -8)])
+    assert np.array_equal(_bits_rne_bf16(ties), [1.0, 1 + 2.0 ** -6, -1.0])
+
+
+def test_store_bf16_is_identity_on_representable_values():
+    """x in {-1, 0, 1}, weights in {0, +-1/2}, no bias: every q, k, v is a
+    small multiple of 1/2, exactly representable in bf16, so rounding the
+    stored qkv changes nothing (bitwise)."""
+    rng = np.random.default_rng(3)
+    B, T, C, H = 2, 8, 16, 2
+    import dataclasses
+    inp = make_inputs(B, T, C, H, bias=False, dtype="f32", seed=1)
+    inp = dataclasses.replace(
+        inp, x=rng.integers(-1, 2, (B, T, C)).astype(np.float32),
+        W_attn=(rng.integers(-1, 2, (C, 3 * C)) * 0.5).astype(np.float32))
+    a = fwd(inp)["y"]
+    b = oracle.forward(inp.x, inp.W_attn, None, inp.W_proj, None, H,
+                       store_bf16=("qkv",))["y"]
+    assert np.array_equal(a, b)
+
+
+def test_backward_store_bf16_rounds_exactly_the_stored_tensors():
+    """Rounding a stored gradient changes nothing upstream of it, and the
+    gradients downstream are the exact chain rule through the rounded
+    values (checked with plain fp64 matrix products)."""
+    B, T, C, H = 2, 9, 16, 2
+    inp = make_inputs(B, T, C, H, dtype="f32", seed=12, w_std=0.4, proj_std=0.4, with_dY=True)
+    args = (inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, H)
+    ex = oracle.backward(*args, want_inter=True)
+    rd = oracle.backward(*args, want_inter=True, store_bf16=("dqkv",))
+    assert np.array_equal(rd["dqkv"], _bits_rne_bf16(ex["dqkv"]))
+    assert np.array_equal(rd["dym"], ex["dym"])
+    x = inp.x.reshape(-1, C).astype(np.float64)
+    g = rd["dqkv"].reshape(-1, 3 * C)
+    np.testing.assert_allclose(rd["dW_attn"], x.T @ g, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(rd["db_attn"], g.sum(0), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(rd["dx"].reshape(-1, C), g @ inp.W_attn.T.astype(np.float64),
+                               rtol=1e-12, atol=1e-13)
+    r2 = oracle.backward(*args, want_inter=True, store_bf16=("dym",))
+    assert np.array_equal(r2["dym"], _bits_rne_bf16(ex["dym"]))
+    # stored merged heads: dW_proj = round(ym)^T dY
+    r3 = oracle.backward(*args, store_bf16=("ym",))
+    ym = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, H,
+                        want=("ym",), store_bf16=("ym",))["ym"].reshape(-1, C)
+    np.testing.assert_allclose(r3["dW_proj"], ym.T @ inp.dY.reshape(-1, C).astype(np.float64),
+                               rtol=1e-12, atol=1e-13)
+    # no rounding requested: bitwise the plain backward
+    r4 = oracle.backward(*args, want_inter=True, store_bf16=())
+    for k in ex:
+        assert np.array_equal(r4[k], ex[k])
