@@ -1,0 +1,384 @@
+// gemm2.cuh -- pipelined bf16 MFMA GEMM for gfx950.
+//
+// C[m][n] = sum_k A(m,k) B(k,n) with fp32 accumulation, handed to an epilogue
+// in runs of 4 consecutive columns.  Operand layouts (template flags):
+//   A_KC: A(m,k) = A[m*lda + k]  (k contiguous)   else A(m,k) = A[k*lda + m]
+//   B_KC: B(k,n) = B[n*ldb + k]  (k contiguous)   else B(k,n) = B[k*ldb + n]
+//
+// Data movement.  Operand tiles go from global memory straight into LDS with
+// global_load_lds_dwordx4 (no register staging), into an NSTAGE-deep ring:
+// the loads for k-tile kt+NSTAGE-1 are in flight while tile kt is multiplied.
+// Each wave waits only for its own oldest loads (s_waitcnt vmcnt(n)) and a
+// bare s_barrier publishes the tile; no fence drains the ring.
+//
+// LDS layouts (16-byte chunks, XOR-swizzled so MFMA operand reads spread over
+// the banks):
+//   k-contiguous operand: [row][BK], chunk c of row r at slot c ^ (r & 7);
+//     an MFMA fragment (32 rows x 16 k) is one ds_read_b128 per lane.
+//   row-contiguous operand: [BK][ROWS], chunk c of k-row r at slot
+//     c ^ 4*(r & 3); a fragment is two ds_read_b64_tr_b16 per lane.  Within a
+//     group of 16 lanes that instruction hands output lane j element e =
+//     the (j%4)-th 16-bit value fetched by source lane 4e + j/4; so source lane
+//     s pointing at row kb + s/4, column nb + 4(s%4) delivers to lane j the
+//     four k values kb..kb+3 of column nb + j -- the MFMA operand layout.
+//
+// MFMA.  v_mfma_f32_32x32x16_bf16 with the operands swapped (B fragment as
+// the "A" input), so each accumulator tile is D^T: lane l holds row
+// m = l%32 and, in register group g, the four consecutive columns
+// 8g + 4(l/32) + 0..3 -- stored directly as 8 (bf16) or 16 (fp32) bytes.
+//
+// WGM x WGN waves (64 threads each); block tile BM x BN; split-K over
+// grid.y.  Chunks outside the matrix (ragged M, N or K) read a 16-byte zero
+// block.  Requires N % 8 == 0, K % 8 == 0 for a k-contiguous operand and the
+// row count % 8 == 0 for a row-contiguous one.
+#pragma once
+
+#include "common.cuh"
+#include "gemm.cuh"
+
+namespace gpt_attn {
+
+__device__ __align__(16) static const uint4 g_zero16 = {0u, 0u, 0u, 0u};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+#define GA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define GA_LDS4(p) ((__attribute__((address_space(3))) v4i16*)(p))
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_barrier without a memory fence (the ring is published by the waits
+// above), fenced against compiler reordering of LDS accesses.
+__device__ __forceinline__ void bar_nofence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int BK, int NSTAGE, bool A_KC, bool B_KC, int NW = 4>
+struct Gemm2Cfg {
+  static_assert(BK == 64 || BK == 32, "BK");
+  static constexpr int kA = BM * BK * 2;            // bytes of one A stage
+  static constexpr int kB = BN * BK * 2;            // bytes of one B stage
+  static constexpr int kStage = kA + kB;
+  static constexpr int kSmem = NSTAGE * kStage;
+  static constexpr int kLoadsA = kA / 1024 / NW;    // 1 KB loads per wave
+  static constexpr int kLoadsB = kB / 1024 / NW;
+  static constexpr int kLoads = kLoadsA + kLoadsB;  // per wave per stage
+  static_assert(kA % (1024 * NW) == 0 && kB % (1024 * NW) == 0, "tile too small");
+  static_assert(kLoads * (NSTAGE - 1) < 64, "vmcnt range");
+  static_assert(kSmem <= 160 * 1024, "LDS");
+};
+
+// Issue the global->LDS loads of one operand tile (ROWS x BK) for this wave.
+// KC: source (row, k) at src[row*ld + k]; RC: at src[k*ld + row].
+// Slot swizzle of a k-contiguous tile: chunk c of row r lives at c ^ kc_swz(r).
+// BK = 64 (8 chunks a row): r & 7.  BK = 32 (4 chunks): (r >> 1) & 3, so the
+// 64-byte rows of 8 consecutive rows cover distinct bank groups.
+template <int BK>
+__device__ __forceinline__ int kc_swz(int row) {
+  return BK == 64 ? (row & 7) : ((row >> 1) & 3);
+}
+
+template <int ROWS, int BK, bool KC>
+__device__ __forceinline__ void g2_issue_check() {
+  static_assert(KC || ROWS >= 128, "row-contiguous operand tiles need >= 128 rows");
+}
+
+template <int ROWS, int BK, bool KC, int NW = 4>
+__device__ __forceinline__ void g2_issue(const bf16_t* __restrict__ src, int ld, int row0,
+                                         int nrows, int k0, int kend, char* lds, int wid,
+                                         int lane) {
+  constexpr int kPerWave = ROWS * BK * 2 / 1024 / NW;
+  g2_issue_check<ROWS, BK, KC>();
+#pragma unroll
+  for (int q = 0; q < kPerWave; ++q) {
+    const int inst = wid * kPerWave + q;  // 1 KB block index within the tile
+    const bf16_t* g;
+    if (KC) {
+      // 1024 / (2 BK) rows of BK k per instruction; lane -> (row, slot)
+      constexpr int CPK = BK / 8;  // chunks per row
+      const int row = inst * (64 / CPK) + lane / CPK;
+      const int slot = lane % CPK;
+      const int chunk = slot ^ kc_swz<BK>(row);
+      const int gr = row0 + row, gk = k0 + chunk * 8;
+      g = (gr < nrows && gk < kend) ? src + (size_t)gr * ld + gk
+                                    : reinterpret_cast<const bf16_t*>(&g_zero16);
+    } else {
+      constexpr int CPR = ROWS / 8;               // chunks per k-row
+      constexpr int RPI = 64 / CPR;               // k-rows per instruction
+      const int krow = inst * RPI + lane / CPR;
+      const int slot = lane % CPR;
+      const int chunk = slot ^ ((krow & 3) << 2);
+      const int gk = k0 + krow, gr = row0 + chunk * 8;
+      g = (gk < kend && gr < nrows) ? src + (size_t)gk * ld + gr
+                                    : reinterpret_cast<const bf16_t*>(&g_zero16);
+    }
+    __builtin_amdgcn_load_to_lds((void*)g, GA_LDS(lds + inst * 1024), 16, 0, 0);
+  }
+}
+
+// MFMA operand fragment: rows rb..rb+31 of the tile, k = 16*kk + 8*(lane/32) + 0..7.
+// (kc_swz, the k-contiguous swizzle, is defined above g2_issue.)
+template <int ROWS, int BK, bool KC>
+__device__ __forceinline__ bf16x8 g2_frag(const char* lds, int rb, int kk, int lane) {
+  if (KC) {
+    const int row = rb + (lane & 31);
+    const int chunk = 2 * kk + (lane >> 5);
+    return *reinterpret_cast<const bf16x8*>(lds + row * (BK * 2) + ((chunk ^ kc_swz<BK>(row)) << 4));
+  } else {
+    const int G = lane >> 4, s = lane & 15;
+    const int h = G >> 1, nsub = G & 1;
+    const int n = rb + 16 * nsub + 4 * (s & 3);
+    const int chunk = n >> 3, half = (n >> 2) & 1;
+    v4i16 r[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int krow = 16 * kk + 8 * h + 4 * t + (s >> 2);
+      const char* p = lds + krow * (ROWS * 2) + ((chunk ^ ((krow & 3) << 2)) << 4) + half * 8;
+      r[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(GA_LDS4(p));
+    }
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    v8i16 c = {r[0][0], r[0][1], r[0][2], r[0][3], r[1][0], r[1][1], r[1][2], r[1][3]};
+    return __builtin_bit_cast(bf16x8, c);
+  }
+}
+
+// Epilogues receive (m, n, v[4]) for columns n..n+3 (n % 4 == 0).
+struct Epi2RowMajor {
+  bf16_t* out;
+  int ldc;
+  const bf16_t* bias;  // may be NULL
+  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
+    float b[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+      const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
+      b[0] = bf2f(u.x & 0xffff); b[1] = bf2f(u.x >> 16);
+      b[2] = bf2f(u.y & 0xffff); b[3] = bf2f(u.y >> 16);
+    }
+    uint2 w;
+    w.x = pack_bf16x2(v[0] + b[0], v[1] + b[1]);
+    w.y = pack_bf16x2(v[2] + b[2], v[3] + b[3]);
+    *reinterpret_cast<uint2*>(out + (size_t)m * ldc + n) = w;
+  }
+  // staged path: bias is added before rounding into the LDS tile
+  static constexpr bool kStaged = true;
+  __device__ __forceinline__ float bias_at(int n) const { return bias ? bf2f(bias[n]) : 0.f; }
+  __device__ __forceinline__ void store8(int m, int n, uint4 w) const {
+    *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = w;
+  }
+};
+
+// c_attn epilogue: bias, rounding, and the scatter of column n of row
+// m = b*T + t to qkv[s][b][h][t][d] (s = n / C, h = (n % C) / hs, d = n % hs).
+// The kernel asks for row and column offsets once per 32-row / 32-column
+// block (hs is a multiple of 32, so a 32-column block lies in one head) and
+// adds the per-lane remainder.
+struct Epi2QKV {
+  bf16_t* qkv;
+  const bf16_t* bias;  // [3C] or NULL
+  int B, T, C, H, hs;
+  static constexpr bool kSplitOffsets = true;
+  __device__ __forceinline__ size_t row_off(int m) const {  // (b, t) part
+    const int bb = m / T, t = m - bb * T;
+    return ((size_t)bb * H * T + t) * hs;
+  }
+  __device__ __forceinline__ size_t col_off(int n) const {  // (s, h, d) part
+    const int s = n / C, rem = n - s * C;
+    const int h = rem / hs, d = rem - h * hs;
+    return (size_t)s * B * H * T * hs + (size_t)h * T * hs + d;
+  }
+  __device__ __forceinline__ void store(size_t off, int n, const float* v) const {
+    float b[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+      const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
+      b[0] = bf2f(u.x & 0xffff); b[1] = bf2f(u.x >> 16);
+      b[2] = bf2f(u.y & 0xffff); b[3] = bf2f(u.y >> 16);
+    }
+    uint2 w;
+    w.x = pack_bf16x2(v[0] + b[0], v[1] + b[1]);
+    w.y = pack_bf16x2(v[2] + b[2], v[3] + b[3]);
+    *reinterpret_cast<uint2*>(qkv + off) = w;
+  }
+  static constexpr bool kStaged = true;
+  __device__ __forceinline__ float bias_at(int n) const { return bias ? bf2f(bias[n]) : 0.f; }
+  __device__ __forceinline__ void store8(int m, int n, uint4 w) const {
+    *reinterpret_cast<uint4*>(qkv + row_off(m) + col_off(n)) = w;
+  }
+};
+
+template <class Epi, class = void>
+struct Staged { static constexpr bool value = false; };
+template <class Epi>
+struct Staged<Epi, decltype(void(Epi::kStaged))> { static constexpr bool value = Epi::kStaged; };
+
+template <class Epi, class = void>
+struct SplitOffsets { static constexpr bool value = false; };
+template <class Epi>
+struct SplitOffsets<Epi, decltype(void(Epi::kSplitOffsets))> {
+  static constexpr bool value = Epi::kSplitOffsets;
+};
+
+struct Epi2Partial {
+  float* part;
+  int ldc;
+  size_t split_stride;
+  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
+    *reinterpret_cast<float4*>(part + (size_t)blockIdx.y * split_stride + (size_t)m * ldc + n) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+template <int BM, int BN, int BK, int NSTAGE, bool A_KC, bool B_KC, int WGM, int WGN, class Epi>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(
+    const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ Bm, int ldb, int M, int N,
+    int K, int k_split, Epi epi) {
+  constexpr int NW = WGM * WGN;
+  using Cfg = Gemm2Cfg<BM, BN, BK, NSTAGE, A_KC, B_KC, NW>;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MT = WTM / 32, NT = WTN / 32;
+  __shared__ __align__(1024) char smem[Cfg::kSmem];
+
+  const int tiles_n = (N + BN - 1) / BN;
+  const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
+  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WGN, wn = wid % WGN;
+  const int kbeg = (int)blockIdx.y * k_split;
+  const int kend = min(K, kbeg + k_split);
+  const int nk = (kend - kbeg + BK - 1) / BK;
+
+  auto issue = [&](int stage, int kt) {
+    char* sa = smem + stage * Cfg::kStage;
+    g2_issue<BM, BK, A_KC, NW>(A, lda, m0, M, kbeg + kt * BK, kend, sa, wid, lane);
+    g2_issue<BN, BK, B_KC, NW>(Bm, ldb, n0, N, kbeg + kt * BK, kend, sa + Cfg::kA, wid, lane);
+  };
+
+  floatx16 acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+#pragma unroll
+  for (int s = 0; s < NSTAGE - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // tile kt is complete once at most (later tiles issued) x loads remain
+    const int later = min(nk - 1, kt + NSTAGE - 2) - kt;
+    if (later >= NSTAGE - 2) wait_vmcnt<Cfg::kLoads * (NSTAGE - 2)>();
+    else if (NSTAGE > 3 && later == 2) wait_vmcnt<Cfg::kLoads * 2>();
+    else if (later == 1) wait_vmcnt<Cfg::kLoads>();
+    else wait_vmcnt<0>();
+    bar_nofence();
+    if (kt + NSTAGE - 1 < nk) issue((kt + NSTAGE - 1) % NSTAGE, kt + NSTAGE - 1);
+    const char* sa = smem + (kt % NSTAGE) * Cfg::kStage;
+    const char* sb = sa + Cfg::kA;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 af[MT], bfr[NT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) af[i] = g2_frag<BM, BK, A_KC>(sa, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) bfr[j] = g2_frag<BN, BK, B_KC>(sb, wn * WTN + j * 32, kk, lane);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
+    }
+  }
+
+  if constexpr (Staged<Epi>::value && BM * (BN + 8) * 2 <= Cfg::kSmem) {
+    // ---- staged epilogue: bias + bf16 rounding into an LDS tile [BM][BN+8],
+    // then every 8 lanes store one 128-byte run of a row.
+    constexpr int SP = BN + 8;  // pitch (elements); 16-byte aligned rows
+    bf16_t* ct = reinterpret_cast<bf16_t*>(smem);
+    bar_nofence();  // every wave is done with the operand ring
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int cl = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);  // local column
+        const int n = n0 + cl;
+        float b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = (n + e < N) ? epi.bias_at(n + e) : 0.f;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const int rl = wm * WTM + i * 32 + (lane & 31);
+          uint2 w;
+          w.x = pack_bf16x2(acc[i][j][4 * g] + b[0], acc[i][j][4 * g + 1] + b[1]);
+          w.y = pack_bf16x2(acc[i][j][4 * g + 2] + b[2], acc[i][j][4 * g + 3] + b[3]);
+          *reinterpret_cast<uint2*>(ct + rl * SP + cl) = w;
+        }
+      }
+    bar_nofence();
+    constexpr int kChunks = BM * BN / 8;
+    for (int c = tid; c < kChunks; c += 64 * NW) {
+      const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+      const int m = m0 + rl, n = n0 + cl;
+      if (m < M && n < N) epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
+    }
+    return;
+  }
+  // ---- epilogue straight from the D^T accumulators
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+    if (m >= M) continue;
+    if constexpr (SplitOffsets<Epi>::value) {
+      const size_t ro = epi.row_off(m);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int nb = n0 + wn * WTN + j * 32;
+        if (nb >= N) continue;
+        const size_t co = epi.col_off(nb);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int dn = 8 * g + 4 * (lane >> 5);
+          const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                              acc[i][j][4 * g + 3]};
+          epi.store(ro + co + dn, nb + dn, v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+          if (n < N) {
+            const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                acc[i][j][4 * g + 3]};
+            epi(m, n, v);
+          }
+        }
+    }
+  }
+}
+
+// splits > 1 divides K into that many slices (multiples of BK); returns the
+// number of slices launched.
+template <int BM, int BN, int NSTAGE, int BK, int WGM, int WGN, bool A_KC, bool B_KC, class Epi>
+inline int launch_gemm2(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N,
+                        int K, const Epi& epi, hipStream_t st, int splits = 1) {
+  const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (grid == 0 || K <= 0) return 0;
+  if (splits < 1) splits = 1;
+  int k_split = (K + splits - 1) / splits;
+  k_split = (k_split + BK - 1) / BK * BK;
+  const int ns = (K + k_split - 1) / k_split;
+  hipLaunchKernelGGL((gemm2_kernel<BM, BN, BK, NSTAGE, A_KC, B_KC, WGM, WGN, Epi>),
+                     dim3(grid, ns), dim3(64 * WGM * WGN), 0, st, A, lda, B, ldb, M, N, K,
+                     k_split, epi);
+  return ns;
+}
+
+}  // namespace gpt_attn

@@ -15,6 +15,22 @@
 #include "attn_bwd.cuh"
 #include "attn_fwd.cuh"
 #include "gemm.cuh"
+#include "gemm2.cuh"
+
+// Tile shapes (BM, BN, pipeline stages, BK, wave grid rows, wave grid columns)
+// of the bf16 GEMMs.
+#ifndef GA_QKV_TILE
+#define GA_QKV_TILE 256, 256, 2, 64, 2, 4
+#endif
+#ifndef GA_PROJ_TILE
+#define GA_PROJ_TILE 192, 256, 2, 64, 2, 4
+#endif
+#ifndef GA_DGRAD_TILE
+#define GA_DGRAD_TILE 192, 256, 2, 64, 2, 4
+#endif
+#ifndef GA_WGRAD_TILE
+#define GA_WGRAD_TILE 128, 128, 2, 64, 2, 2
+#endif
 
 using namespace gpt_attn;
 
@@ -233,10 +249,10 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
     const bf16_t* xb = (const bf16_t*)x;
     bf16_t* qkv = (bf16_t*)h->qkv;
     bf16_t* o = (bf16_t*)h->o;
-    EpiQKV<bf16_t> e1{qkv, (const bf16_t*)b_attn, B, T, C, H, hs};
+    Epi2QKV e1{qkv, (const bf16_t*)b_attn, B, T, C, H, hs};
     mark(h, 0, st);
-    launch_gemm_bf16<128, 128, true, false>(xb, C, (const bf16_t*)W_attn, 3 * C, M, 3 * C, C,
-                                            e1, st);
+    launch_gemm2<GA_QKV_TILE, true, false>(xb, C, (const bf16_t*)W_attn, 3 * C, M, 3 * C, C, e1,
+                                           st);
     mark(h, 1, st);
     const dim3 agrid(B * H, (T + kAttnBQ - 1) / kAttnBQ);
     if (hs == 64)
@@ -246,8 +262,8 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
       hipLaunchKernelGGL(attn_fwd_bf16_kernel<32>, agrid, dim3(256), 0, st, qkv,
                          qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
     mark(h, 2, st);
-    EpiRowMajor<bf16_t> e3{(bf16_t*)y, C, (const bf16_t*)b_proj};
-    launch_gemm_bf16<128, 128, true, false>(o, C, (const bf16_t*)W_proj, C, M, C, C, e3, st);
+    Epi2RowMajor e3{(bf16_t*)y, C, (const bf16_t*)b_proj};
+    launch_gemm2<GA_PROJ_TILE, true, false>(o, C, (const bf16_t*)W_proj, C, M, C, C, e3, st);
     mark(h, 3, st);
   } else {
     const float* xf = (const float*)x;
@@ -343,13 +359,13 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     bf16_t* dym = (bf16_t*)h->dym;
     bf16_t* dqkv = (bf16_t*)h->dqkv;
     // ---- c_proj: dym = dY W_proj^T ; dW_proj = ym^T dY ; db_proj = colsum(dY)
-    EpiRowMajor<bf16_t> e_dym{dym, C, nullptr};
-    launch_gemm_bf16<128, 128, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M, C,
-                                           C, e_dym, st);
-    EpiPartial e_wp{part, C, (size_t)C * C};
+    Epi2RowMajor e_dym{dym, C, nullptr};
+    launch_gemm2<GA_DGRAD_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M, C,
+                                            C, e_dym, st);
+    Epi2Partial e_wp{part, C, (size_t)C * C};
     const int s1 = splits_for(((C + 127) / 128) * ((C + 127) / 128));
-    const int n1 = launch_gemm_bf16<128, 128, false, false>(o, C, (const bf16_t*)dY, C, C, C, M,
-                                                            e_wp, st, s1);
+    const int n1 = launch_gemm2<GA_WGRAD_TILE, false, false>(o, C, (const bf16_t*)dY, C, C, C, M,
+                                                             e_wp, st, s1);
     hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(rblocks), dim3(256), 0, st, part, n1,
                        (size_t)C * C, (size_t)C * C, (bf16_t*)dW_proj);
     if (db_proj) {
@@ -383,13 +399,13 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     }
     mark(h, 6, st);
     // ---- c_attn: dx = dqkv W_attn^T ; dW_attn = x^T dqkv ; db_attn = colsum(dqkv)
-    EpiRowMajor<bf16_t> e_dx{(bf16_t*)dx, C, nullptr};
-    launch_gemm_bf16<128, 128, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3, e_dx,
-                                           st);
-    EpiPartial e_wa{part, N3, (size_t)C * N3};
+    Epi2RowMajor e_dx{(bf16_t*)dx, C, nullptr};
+    launch_gemm2<GA_DGRAD_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3, e_dx,
+                                            st);
+    Epi2Partial e_wa{part, N3, (size_t)C * N3};
     const int s2 = splits_for(((C + 127) / 128) * ((N3 + 127) / 128));
-    const int n2 = launch_gemm_bf16<128, 128, false, false>((const bf16_t*)x, C, dqkv, N3, C, N3,
-                                                            M, e_wa, st, s2);
+    const int n2 = launch_gemm2<GA_WGRAD_TILE, false, false>((const bf16_t*)x, C, dqkv, N3, C, N3,
+                                                             M, e_wa, st, s2);
     hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(rblocks), dim3(256), 0, st, part, n2,
                        (size_t)C * N3, (size_t)C * N3, (bf16_t*)dW_attn);
     if (db_attn) {
