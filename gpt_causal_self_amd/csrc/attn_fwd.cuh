@@ -26,7 +26,10 @@
 // thread, key/value tiles in LDS, online softmax key by key.
 #pragma once
 
+#include <type_traits>
+
 #include "common.cuh"
+#include "gemm2.cuh"
 
 namespace gpt_attn {
 
@@ -219,6 +222,247 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
   if (myq < T) {
     const float inv = 1.f / l;
     const int C = HS * H_;
+    bf16_t* orow = O + ((size_t)b * T + myq) * C + h * HS;
+#pragma unroll
+    for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * hi;
+        uint2 w;
+        w.x = pack_bf16x2(acc[dt][4 * g + 0] * inv, acc[dt][4 * g + 1] * inv);
+        w.y = pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d0) = w;
+      }
+    if (lse != nullptr && hi == 0)
+      lse[(size_t)bh * T + myq] = (m + __log2f(l)) * 0.69314718055994530942f;
+  }
+}
+
+// ----------------------------------------------------- bf16, pipelined
+// Second-generation bf16 kernel (the one the library launches).  Same wave
+// decomposition and S^T = K Q^T formulation as above, with:
+//  * K and V tiles moved global -> LDS by global_load_lds_dwordx4 into an
+//    NS-stage ring (manual vmcnt waits, bare barriers), rows of hs elements
+//    with 16-byte chunks XOR-swizzled by the key row;
+//  * the V^T MFMA operand read with ds_read_b64_tr_b16 straight from the
+//    [key][d] tile, in the permuted key order of the probability registers
+//    (no register transposition);
+//  * the score scale folded into the exp2 argument with one FMA, and lazy
+//    rescaling: the running reference max only moves (rescaling l and the
+//    accumulators) when a tile's max exceeds it by more than 8 in log2 units,
+//    so probabilities stay <= 2^8 and most tiles skip the rescale.
+template <int HS>
+__device__ __forceinline__ int kv_swz(int row) {
+  return HS == 64 ? (row & 7) : ((row >> 1) & 3);
+}
+
+template <int HS, int NS>
+__global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kg,
+    const bf16_t* __restrict__ Vg, bf16_t* __restrict__ O, float* __restrict__ lse,
+    int H, int T, float scale_log2) {
+  static_assert(HS == 32 || HS == 64, "head size");
+  constexpr int BKV = kAttnBK;
+  constexpr int TILE = BKV * HS * 2;   // bytes of one K or V tile
+  constexpr int STAGE = 2 * TILE;
+  constexpr int RB = HS * 2;           // bytes of one key row
+  constexpr int CPR = HS / 8;          // 16-byte chunks per key row
+  constexpr int RPI = 64 / CPR;        // key rows per 1 KB load
+  constexpr int LPW = TILE / 1024 / 4; // loads per wave per tile (K or V)
+  constexpr int kLoads = 2 * LPW;
+  constexpr float kLazy = 8.f;         // rescale threshold (log2 units)
+  __shared__ __align__(1024) char smem[NS * STAGE];
+
+  const int nqt = (T + kAttnBQ - 1) / kAttnBQ;
+  const int bh = blockIdx.x;
+  const int qt = nqt - 1 - (int)blockIdx.y;  // heavy tiles first
+  const int b = bh / H, h = bh - b * H;
+  const size_t head = (size_t)bh * T * HS;
+  const bf16_t* Qh = Q + head;
+  const bf16_t* Kh = Kg + head;
+  const bf16_t* Vh = Vg + head;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int hi = lane >> 5;
+  const int q0 = qt * kAttnBQ + wid * 32;
+  const int myq = q0 + (lane & 31);
+
+  bf16x8 qf[HS / 16];
+#pragma unroll
+  for (int kk = 0; kk < HS / 16; ++kk)
+    qf[kk] = myq < T ? *reinterpret_cast<const bf16x8*>(Qh + (size_t)myq * HS + 16 * kk + 8 * hi)
+                     : bf16x8{};
+  floatx16 acc[HS / 32];
+#pragma unroll
+  for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  // Loop-invariant LDS offsets.  K fragment (row kt*32 + lane%32, chunk
+  // 2kk + hi): the row's swizzle is (lane & 7) for every kt (rows differ by
+  // multiples of 8), so only kk and the lane matter.  V transposing reads
+  // (row kb + 8t + 4(G/2) + s/4, column dt*32 + 16(G%2) + 4(s%4)): kb + 8t is
+  // a multiple of 8, so the swizzle depends on the lane part r0 only.
+  int koff[HS / 16];
+#pragma unroll
+  for (int kk = 0; kk < HS / 16; ++kk) {
+    const int row = lane & 31;
+    koff[kk] = row * RB + (((2 * kk + hi) ^ kv_swz<HS>(row)) << 4);
+  }
+  const int G = lane >> 4, s16 = lane & 15;
+  const int r0 = 4 * (G >> 1) + (s16 >> 2);
+  int voff[HS / 32];
+#pragma unroll
+  for (int dt = 0; dt < HS / 32; ++dt) {
+    const int d = dt * 32 + 16 * (G & 1) + 4 * (s16 & 3);
+    voff[dt] = r0 * RB + (((d >> 3) ^ kv_swz<HS>(r0)) << 4) + ((d >> 2) & 1) * 8;
+  }
+
+  const int kv_end = min(T, (qt + 1) * kAttnBQ);
+  const int nkv = (kv_end + BKV - 1) / BKV;
+
+  auto issue = [&](int stage, int j0) {
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int inst = wid * LPW + q;
+      const int row = inst * RPI + lane / CPR;
+      const int chunk = (lane % CPR) ^ kv_swz<HS>(row);
+      const int key = j0 + row;
+      const bool ok = key < T;
+      const bf16_t* gk = ok ? Kh + (size_t)key * HS + chunk * 8
+                            : reinterpret_cast<const bf16_t*>(&g_zero16);
+      const bf16_t* gv = ok ? Vh + (size_t)key * HS + chunk * 8
+                            : reinterpret_cast<const bf16_t*>(&g_zero16);
+      char* base = smem + stage * STAGE + inst * 1024;
+      __builtin_amdgcn_load_to_lds((void*)gk, GA_LDS(base), 16, 0, 0);
+      __builtin_amdgcn_load_to_lds((void*)gv, GA_LDS(base + TILE), 16, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nkv) issue(s, s * BKV);
+
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) const bf16x8 lds_b128;
+  const lds_char* lbase = (const lds_char*)smem;
+
+  // One 64-key tile.  MASK: apply the causal mask (diagonal tiles).
+  auto tile = [&](auto mask_tag, int stage_off, int j0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // ---- S^T = K Q^T for keys j0 .. j0+63
+    int ka[HS / 16];
+#pragma unroll
+    for (int kk = 0; kk < HS / 16; ++kk) ka[kk] = stage_off + koff[kk];
+    floatx16 sc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kt][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < HS / 16; ++kk) {
+        const bf16x8 kf = *(lds_b128*)(lbase + ka[kk] + kt * 32 * RB);
+        sc[kt] = mfma32(kf, qf[kk], sc[kt]);
+      }
+    }
+    if constexpr (MASK) {
+      // key - myq = (j0 - q0) + kt*32 + 8(r/4) + 4hi + r%4 - lane%32
+      const int lim = myq - j0 - 4 * hi;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) sc[kt][r] = -INFINITY;
+    }
+    float smax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sc[kt][r]);
+    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    const float tmax = smax * scale_log2;
+    // ---- lazy rescale (wave-uniform branch)
+    const bool need = tmax > m + kLazy;
+    if (__any(need)) {
+      const float m_new = need ? tmax : m;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
+    // ---- probabilities (relative to m, at most 2^8), row sum
+    const float negm = -m;
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][r], scale_log2, negm));
+        sc[kt][r] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 32);
+    l += rs;
+    // ---- O^T += V^T P^T; V^T operand by transposing reads in the key order
+    // of the P registers: element e <-> key kb + 8(e/4) + 4*hi + e%4.
+    int va[HS / 32];
+#pragma unroll
+    for (int dt = 0; dt < HS / 32; ++dt) va[dt] = stage_off + TILE + voff[dt];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[e] = (__bf16)sc[kt][8 * u + e];
+        const int kb = kt * 32 + 16 * u;
+#pragma unroll
+        for (int dt = 0; dt < HS / 32; ++dt) {
+          v4i16 rv[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            rv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(lbase + va[dt] + (kb + 8 * t) * RB));
+          typedef short v8i16 __attribute__((ext_vector_type(8)));
+          const v8i16 vv = {rv[0][0], rv[0][1], rv[0][2], rv[0][3],
+                            rv[1][0], rv[1][1], rv[1][2], rv[1][3]};
+          acc[dt] = mfma32(__builtin_bit_cast(bf16x8, vv), pf, acc[dt]);
+        }
+      }
+  };
+
+  // Ring step: wait for tile `it`, publish it, refill the ring.
+  auto step = [&](int it) {
+    const int later = min(nkv - 1, it + NS - 2) - it;
+    if (later >= NS - 2) wait_vmcnt<kLoads * (NS - 2)>();
+    else if (NS > 3 && later == 2) wait_vmcnt<kLoads * 2>();
+    else if (later == 1) wait_vmcnt<kLoads>();
+    else wait_vmcnt<0>();
+    bar_nofence();
+    if (it + NS - 1 < nkv) issue((it + NS - 1) % NS, (it + NS - 1) * BKV);
+  };
+  // Tiles wholly below the block's first query need no mask for any wave;
+  // the last (at most two) tiles reach the diagonal.
+  const int n_full = min(nkv, (qt * kAttnBQ) / BKV);
+  int it = 0;
+  for (; it < n_full; ++it) {
+    step(it);
+    tile(std::integral_constant<bool, false>{}, (it % NS) * STAGE, it * BKV);
+  }
+  for (; it < nkv; ++it) {
+    step(it);
+    const int j0 = it * BKV;
+    if (j0 <= q0 + 31)  // skip tiles wholly in this wave's future
+      tile(std::integral_constant<bool, true>{}, (it % NS) * STAGE, j0);
+  }
+
+  if (myq < T) {
+    const float inv = 1.f / l;
+    const int C = HS * H;
     bf16_t* orow = O + ((size_t)b * T + myq) * C + h * HS;
 #pragma unroll
     for (int dt = 0; dt < HS / 32; ++dt)

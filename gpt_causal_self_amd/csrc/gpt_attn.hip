@@ -28,6 +28,9 @@
 #ifndef GA_DGRAD_TILE
 #define GA_DGRAD_TILE 192, 256, 2, 64, 2, 4
 #endif
+#ifndef GA_ATTN_STAGES
+#define GA_ATTN_STAGES 3
+#endif
 #ifndef GA_WGRAD_TILE
 #define GA_WGRAD_TILE 128, 128, 2, 64, 2, 2
 #endif
@@ -256,11 +259,11 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
     mark(h, 1, st);
     const dim3 agrid(B * H, (T + kAttnBQ - 1) / kAttnBQ);
     if (hs == 64)
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, agrid, dim3(256), 0, st, qkv,
-                         qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
+      hipLaunchKernelGGL((attn_fwd2_bf16_kernel<64, GA_ATTN_STAGES>), agrid, dim3(256), 0, st,
+                         qkv, qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
     else
-      hipLaunchKernelGGL(attn_fwd_bf16_kernel<32>, agrid, dim3(256), 0, st, qkv,
-                         qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
+      hipLaunchKernelGGL((attn_fwd2_bf16_kernel<32, GA_ATTN_STAGES>), agrid, dim3(256), 0, st,
+                         qkv, qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
     mark(h, 2, st);
     Epi2RowMajor e3{(bf16_t*)y, C, (const bf16_t*)b_proj};
     launch_gemm2<GA_PROJ_TILE, true, false>(o, C, (const bf16_t*)W_proj, C, M, C, C, e3, st);
