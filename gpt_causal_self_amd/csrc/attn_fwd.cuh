@@ -384,7 +384,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     const float tmax = smax * scale_log2;
     // ---- lazy rescale (wave-uniform branch)
     const bool need = tmax > m + kLazy;
+#ifdef GA_ATTN_EAGER_RESCALE
+    {
+#else
     if (__any(need)) {
+#endif
       const float m_new = need ? tmax : m;
       const float alpha = need ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
       m = m_new;

@@ -29,7 +29,7 @@
 #define GA_DGRAD_TILE 192, 256, 2, 64, 2, 4
 #endif
 #ifndef GA_ATTN_STAGES
-#define GA_ATTN_STAGES 3
+#define GA_ATTN_STAGES 2
 #endif
 #ifndef GA_WGRAD_TILE
 #define GA_WGRAD_TILE 128, 128, 2, 64, 2, 2

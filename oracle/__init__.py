@@ -50,6 +50,13 @@ def _declare(lib):
     lib.oracle_forward.restype = i
     lib.oracle_forward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
                                    dp, dp, dp, dp, i, i]
+    lib.oracle_layernorm.restype = i
+    lib.oracle_layernorm.argtypes = [i, i, dp, dp, dp, dp, i]
+    lib.oracle_block_attn_forward.restype = i
+    lib.oracle_block_attn_forward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp,
+                                              dp, i, i]
+    lib.oracle_mlp_forward.restype = i
+    lib.oracle_mlp_forward.argtypes = [i, i, i, dp, dp, dp, dp, dp, dp, dp, i, i]
     lib.oracle_backward.restype = i
     lib.oracle_backward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
                                     dp, dp, dp, dp, dp, dp, dp, i, i]
@@ -164,3 +171,59 @@ def backward(x, W_attn, b_attn, W_proj, b_proj, dY, n_head, *, want_inter=False,
     if rc != 0:
         raise ValueError("oracle_backward failed (bad shape or out of memory)")
     return out
+
+
+def layernorm(x, w, b, *, nthreads=None, lib=None):
+    """LayerNorm over the last axis (biased variance, eps 1e-5), fp64."""
+    lib = lib or load()
+    x = _f64(x)
+    C = x.shape[-1]
+    out = np.empty_like(x)
+    rc = lib.oracle_layernorm(int(x.size // C), C, _ptr(x), _ptr(_f64(w)), _ptr(_f64(b)),
+                              _ptr(out), int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_layernorm failed")
+    return out
+
+
+def block_attn_forward(x, ln_w, ln_b, W_attn, b_attn, W_proj, b_proj, n_head, *,
+                       want_ln=False, store_bf16=(), nthreads=None, lib=None):
+    """Attention half of a Pre-LN block: x + layer(ln_1(x)), fp64.
+    ``store_bf16`` may name "ln", "qkv", "ym"."""
+    lib = lib or load()
+    x = _f64(x)
+    B, T, C = x.shape
+    ln_w, ln_b, W_attn, b_attn, W_proj, b_proj = map(
+        _f64, (ln_w, ln_b, W_attn, b_attn, W_proj, b_proj))
+    out = np.empty((B, T, C))
+    ln = np.empty((B, T, C)) if want_ln else None
+    bits = ((1 if "qkv" in store_bf16 else 0) | (2 if "ym" in store_bf16 else 0) |
+            (16 if "ln" in store_bf16 else 0))
+    rc = lib.oracle_block_attn_forward(B, T, C, int(n_head), _ptr(x), _ptr(ln_w), _ptr(ln_b),
+                                       _ptr(W_attn), _ptr(b_attn), _ptr(W_proj), _ptr(b_proj),
+                                       _ptr(out), _ptr(ln), bits,
+                                       int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_block_attn_forward failed")
+    return {"out": out, "ln": ln} if want_ln else {"out": out}
+
+
+def mlp_forward(x, W_fc, b_fc, W_proj, b_proj, *, want_h=False, store_bf16=(),
+                nthreads=None, lib=None):
+    """MLP sublayer c_proj(gelu(c_fc(x))) in fp64; x [..., C]."""
+    lib = lib or load()
+    x = _f64(x)
+    C = x.shape[-1]
+    M = int(x.size // C)
+    W_fc, b_fc, W_proj, b_proj = map(_f64, (W_fc, b_fc, W_proj, b_proj))
+    F = W_fc.shape[1]
+    assert W_fc.shape == (C, F) and W_proj.shape == (F, C)
+    y = np.empty(x.shape)
+    h = np.empty(x.shape[:-1] + (F,)) if want_h else None
+    rc = lib.oracle_mlp_forward(M, C, F, _ptr(x), _ptr(W_fc), _ptr(b_fc), _ptr(W_proj),
+                                _ptr(b_proj), _ptr(y), _ptr(h),
+                                1 if "h" in store_bf16 else 0,
+                                int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_mlp_forward failed")
+    return {"y": y, "h": h} if want_h else {"y": y}

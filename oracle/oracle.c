@@ -24,6 +24,18 @@
  *   Dropout is the identity (dropout 0.0 in GPTConfig, page "nanoGPT global
  *   flow", section 2.1).
  *
+ * Around the layer (the "next" pieces of a Block):
+ *   LayerNorm: (x - mean) / sqrt(var + 1e-5) * w + b over the embedding, with
+ *     the biased variance of F.layer_norm (page "nanoGPT global flow",
+ *     section 2.5 (A));
+ *   attention half of a Pre-LN block: out = x + attn(ln_1(x)) (same page,
+ *     section 2.5, Block.forward; page "nanoGPT architecture explained step
+ *     by step", section 2);
+ *   MLP sublayer: c_proj(gelu(c_fc(x))) with gelu(u) = u * Phi(u), Phi the
+ *     standard normal CDF written with erf (page "nanoGPT architecture
+ *     explained step by step", section 4; page "nanoGPT global flow",
+ *     section 2.5 (C)).
+ *
  * Weights are taken as [in, out] row-major, i.e. the transpose of the
  * nn.Linear storage: y = x . W + b.
  *
@@ -400,5 +412,90 @@ done:
   free(y);
   if (!dym_out) free(dym);
   if (!dqkv_out) free(dqkv);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* LayerNorm, attention half of a Pre-LN block, MLP sublayer.          */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  int C;
+  const double *x, *w, *b;
+  double *out;
+} ln_ctx;
+
+static void ln_row(void *vctx, long m, double *scratch) {
+  (void)scratch;
+  const ln_ctx *c = (const ln_ctx *)vctx;
+  const double *row = c->x + (size_t)m * c->C;
+  double mean = 0.0;
+  for (int i = 0; i < c->C; ++i) mean += row[i];
+  mean /= c->C;
+  double var = 0.0;
+  for (int i = 0; i < c->C; ++i) var += (row[i] - mean) * (row[i] - mean);
+  var /= c->C; /* biased, as F.layer_norm */
+  const double inv = 1.0 / sqrt(var + 1e-5);
+  double *o = c->out + (size_t)m * c->C;
+  for (int i = 0; i < c->C; ++i)
+    o[i] = (row[i] - mean) * inv * c->w[i] + (c->b ? c->b[i] : 0.0);
+}
+
+/* out = LayerNorm(x) row by row; x, out [M][C]; b may be NULL. */
+int oracle_layernorm(int M, int C, const double *x, const double *w, const double *b,
+                     double *out, int nthreads) {
+  if (M < 0 || C <= 0 || !x || !w || !out) return -1;
+  ln_ctx c = {C, x, w, b, out};
+  return parallel_for(M, nthreads, ln_row, &c, 0);
+}
+
+/* Attention half of a Pre-LN block: out = x + layer(ln_1(x)).
+ * store_bf16 bits 0/1 as in oracle_forward; bit 4 rounds the LayerNorm
+ * output (the layer's input) to bfloat16.  ln_out [B][T][C] optional. */
+int oracle_block_attn_forward(int B, int T, int C, int H, const double *x,
+                              const double *ln_w, const double *ln_b,
+                              const double *W_attn, const double *b_attn,
+                              const double *W_proj, const double *b_proj,
+                              double *out, double *ln_out, int store_bf16,
+                              int nthreads) {
+  if (B < 0 || T < 0 || C <= 0 || H <= 0 || C % H != 0 || !x || !ln_w || !out) return -1;
+  const long M = (long)B * T;
+  int rc = -1;
+  double *ln = ln_out ? ln_out : (double *)malloc(((size_t)M * C + 1) * sizeof(double));
+  double *y = (double *)malloc(((size_t)M * C + 1) * sizeof(double));
+  if (!ln || !y) goto done;
+  if (oracle_layernorm((int)M, C, x, ln_w, ln_b, ln, nthreads)) goto done;
+  if (store_bf16 & 16) round_all(ln, (size_t)M * C);
+  if (oracle_forward(B, T, C, H, ln, W_attn, b_attn, W_proj, b_proj, y, NULL, NULL,
+                     NULL, NULL, store_bf16 & 3, nthreads))
+    goto done;
+  for (size_t i = 0; i < (size_t)M * C; ++i) out[i] = x[i] + y[i];
+  rc = 0;
+done:
+  if (!ln_out) free(ln);
+  free(y);
+  return rc;
+}
+
+/* gelu(u) = u * Phi(u) = u * (1 + erf(u / sqrt(2))) / 2 */
+static double gelu(double u) { return u * 0.5 * (1.0 + erf(u / sqrt(2.0))); }
+
+/* MLP sublayer: y = gelu(x . W_fc + b_fc) . W_proj + b_proj.
+ * x [M][C], W_fc [C][F], b_fc [F] or NULL, W_proj [F][C], b_proj [C] or NULL,
+ * y [M][C]; h_out [M][F] (optional) receives gelu's output.  store_bf16 bit
+ * 0 rounds that hidden activation to bfloat16. */
+int oracle_mlp_forward(int M, int C, int F, const double *x, const double *W_fc,
+                       const double *b_fc, const double *W_proj, const double *b_proj,
+                       double *y, double *h_out, int store_bf16, int nthreads) {
+  if (M < 0 || C <= 0 || F <= 0 || !x || !W_fc || !W_proj || !y) return -1;
+  double *h = h_out ? h_out : (double *)malloc(((size_t)M * F + 1) * sizeof(double));
+  if (!h) return -1;
+  int rc = -1;
+  if (linear(M, C, F, x, W_fc, b_fc, h, nthreads)) goto done;
+  for (size_t i = 0; i < (size_t)M * F; ++i) h[i] = gelu(h[i]);
+  if (store_bf16 & 1) round_all(h, (size_t)M * F);
+  if (linear(M, F, C, h, W_proj, b_proj, y, nthreads)) goto done;
+  rc = 0;
+done:
+  if (!h_out) free(h);
   return rc;
 }

@@ -60,6 +60,14 @@ MUTANTS = [
                                      "ldexp(nearbyint(ldexp(f, 7)), e - 7)", 0)]),
     ("bf16 rounding truncates", [("ldexp(nearbyint(ldexp(f, 8)), e - 8)",
                                   "ldexp(trunc(ldexp(f, 8)), e - 8)", 0)]),
+    ("layernorm unbiased variance", [("var /= c->C; /* biased", "var /= (c->C - 1); /* biased", 0)]),
+    ("layernorm without eps", [("1.0 / sqrt(var + 1e-5)", "1.0 / sqrt(var)", 0)]),
+    ("layernorm drops shift", [("+ (c->b ? c->b[i] : 0.0)", "+ 0.0", 0)]),
+    ("gelu tanh approximation",
+     [("return u * 0.5 * (1.0 + erf(u / sqrt(2.0)));",
+       "return u * 0.5 * (1.0 + tanh(0.7978845608028654 * (u + 0.044715 * u * u * u)));", 0)]),
+    ("block drops the residual", [("out[i] = x[i] + y[i];", "out[i] = y[i];", 0)]),
+    ("mlp skips gelu", [("h[i] = gelu(h[i]);", "h[i] = h[i];", 0)]),
     ("input grad with untransposed square weight",
      [("s += g[n] * w[n];",
        "s += g[n] * (c->K == c->N ? c->W[(size_t)n * c->N + k] : w[n]);", 0)]),
@@ -86,6 +94,28 @@ def _pins(lib):
                         want=("qkv",), store_bf16=("qkv",), lib=lib)["qkv"]
     if not np.array_equal(rq, _bits_rne_bf16(ex)):
         failed.append("bf16 rounding")
+    # LayerNorm / MLP / block against torch fp64
+    import torch
+    import torch.nn.functional as F
+    rng = np.random.default_rng(9)
+    xx = rng.standard_normal((6, 16)) * 2 + 1
+    w16, b16 = 1 + 0.1 * rng.standard_normal(16), 0.1 * rng.standard_normal(16)
+    T_ = lambda a: torch.from_numpy(np.asarray(a, np.float64))  # noqa: E731
+    if not np.allclose(oracle.layernorm(xx, w16, b16, lib=lib),
+                       F.layer_norm(T_(xx), (16,), T_(w16), T_(b16), 1e-5).numpy(),
+                       rtol=1e-12, atol=1e-12):
+        failed.append("layernorm")
+    Wf, Wp = rng.standard_normal((16, 64)) * 0.3, rng.standard_normal((64, 16)) * 0.3
+    ym = oracle.mlp_forward(xx, Wf, None, Wp, None, lib=lib)["y"]
+    if not np.allclose(ym, (F.gelu(T_(xx) @ T_(Wf)) @ T_(Wp)).numpy(), rtol=1e-11, atol=1e-13):
+        failed.append("mlp")
+    inb = make_inputs(1, 5, 16, 2, dtype="f32", seed=3, w_std=0.3, proj_std=0.3)
+    ob = oracle.block_attn_forward(inb.x, w16, b16, inb.W_attn, inb.b_attn, inb.W_proj,
+                                   inb.b_proj, 2, lib=lib)["out"]
+    lnb = F.layer_norm(T_(inb.x), (16,), T_(w16), T_(b16), 1e-5).numpy()
+    yb = oracle.forward(lnb, inb.W_attn, inb.b_attn, inb.W_proj, inb.b_proj, 2, lib=lib)["y"]
+    if not np.allclose(ob, inb.x + yb, rtol=1e-12, atol=1e-13):
+        failed.append("block")
     # brute force forward, incl. P and the log-sum-exp
     for (B, T, C, H, bias) in ((2, 5, 8, 2, True), (2, 6, 16, 4, False)):
         inp = make_inputs(B, T, C, H, bias=bias, dtype="f32", seed=T, w_std=0.5,
