@@ -8,9 +8,9 @@
 // transpose + view), never materialising the T x T score matrix.
 //
 // bf16 kernel (MFMA).  One block = 4 waves = 128 queries of one (b, h); each
-// wave owns 32 queries.  Keys and values are streamed through LDS in tiles of
-// 64 (two LDS buffers; the next tile's global loads are issued before the
-// current tile's math).  Per tile a wave computes S^T = K Q^T (keys on the
+// wave owns 32 queries.  Keys and values are streamed through an LDS ring in
+// tiles of 64 (the next tiles' global loads are in flight during the current
+// tile's math).  Per tile a wave computes S^T = K Q^T (keys on the
 // MFMA rows, its 32 queries on the columns) with 32x32x16 bf16 MFMAs, so each
 // lane holds 32 scores of ONE query: the row max / row sum of the online
 // softmax are a local reduction plus one exchange with the other lane half.
@@ -36,211 +36,9 @@ namespace gpt_attn {
 constexpr int kAttnBQ = 128;  // queries per block (bf16 kernel)
 constexpr int kAttnBK = 64;   // keys per tile
 
-template <int HS>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(
-    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kg,
-    const bf16_t* __restrict__ Vg, bf16_t* __restrict__ O, float* __restrict__ lse,
-    int H, int T, float scale_log2) {
-  static_assert(HS == 32 || HS == 64, "head size");
-  constexpr int KP = HS + 8;        // K tile pitch (elements)
-  constexpr int VP = kAttnBK + 4;   // V^T tile pitch (elements)
-  constexpr int KCH = kAttnBK * HS / 8;          // 16-byte chunks per K tile
-  constexpr int KPER = (KCH + 255) / 256;
-  constexpr int VBLK = (kAttnBK / 4) * (HS / 4);  // 4 keys x 4 dims blocks
-  __shared__ __align__(16) bf16_t Ks[2][kAttnBK * KP];
-  __shared__ __align__(16) bf16_t Vt[2][HS * VP];
-
-  const int nqt = (T + kAttnBQ - 1) / kAttnBQ;
-  const int bh = blockIdx.x;
-  const int qt = nqt - 1 - (int)blockIdx.y;  // heavy tiles first
-  const int H_ = H;
-  const int b = bh / H_, h = bh - b * H_;
-  const size_t head = (size_t)bh * T * HS;
-  const bf16_t* Qh = Q + head;
-  const bf16_t* Kh = Kg + head;
-  const bf16_t* Vh = Vg + head;
-
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int hi = lane >> 5;                 // lane half
-  const int q0 = qt * kAttnBQ + wid * 32;   // first query of this wave
-  const int myq = q0 + (lane & 31);
-
-  // Q^T fragments: lane holds q[myq][16*kk + 8*hi + 0..7]
-  bf16x8 qf[HS / 16];
-#pragma unroll
-  for (int kk = 0; kk < HS / 16; ++kk) {
-    if (myq < T)
-      qf[kk] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)myq * HS + 16 * kk + 8 * hi);
-    else
-      qf[kk] = bf16x8{};
-  }
-
-  floatx16 acc[HS / 32];
-#pragma unroll
-  for (int dt = 0; dt < HS / 32; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  float m = -INFINITY, l = 0.f;
-
-  const int kv_end = min(T, (qt + 1) * kAttnBQ);
-  const int nkv = (kv_end + kAttnBK - 1) / kAttnBK;
-
-  // register staging of one K/V tile
-  uint4 kr[KPER];
-  uint2 vr[4];
-  auto gload = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int c = tid + i * 256;
-      const int key = c / (HS / 8), dc = c % (HS / 8);
-      if (c < KCH && j0 + key < T)
-        kr[i] = *reinterpret_cast<const uint4*>(Kh + (size_t)(j0 + key) * HS + dc * 8);
-      else
-        kr[i] = make_uint4(0, 0, 0, 0);
-    }
-    const int dg = tid % (HS / 4), kg = tid / (HS / 4);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int key = j0 + kg * 4 + kk;
-      if (tid < VBLK && key < T)
-        vr[kk] = *reinterpret_cast<const uint2*>(Vh + (size_t)key * HS + dg * 4);
-      else
-        vr[kk] = make_uint2(0, 0);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPER; ++i) {
-      const int c = tid + i * 256;
-      const int key = c / (HS / 8), dc = c % (HS / 8);
-      if (c < KCH) *reinterpret_cast<uint4*>(&Ks[buf][key * KP + dc * 8]) = kr[i];
-    }
-    if (tid < VBLK) {
-      const int dg = tid % (HS / 4), kg = tid / (HS / 4);
-      // transpose 4 keys x 4 dims -> 4 dims x 4 keys
-#pragma unroll
-      for (int dd = 0; dd < 4; ++dd) {
-        const int sh = (dd & 1) * 16;
-        const uint32_t e0 = ((dd < 2 ? vr[0].x : vr[0].y) >> sh) & 0xffffu;
-        const uint32_t e1 = ((dd < 2 ? vr[1].x : vr[1].y) >> sh) & 0xffffu;
-        const uint32_t e2 = ((dd < 2 ? vr[2].x : vr[2].y) >> sh) & 0xffffu;
-        const uint32_t e3 = ((dd < 2 ? vr[3].x : vr[3].y) >> sh) & 0xffffu;
-        uint2 o;
-        o.x = e0 | (e1 << 16);
-        o.y = e2 | (e3 << 16);
-        *reinterpret_cast<uint2*>(&Vt[buf][(dg * 4 + dd) * VP + kg * 4]) = o;
-      }
-    }
-  };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
-  for (int it = 0; it < nkv; ++it) {
-    const int buf = it & 1;
-    const int j0 = it * kAttnBK;
-    if (it + 1 < nkv) gload(j0 + kAttnBK);
-
-    if (j0 <= q0 + 31) {  // some key of the tile is visible to this wave
-      // ---- S^T = K Q^T for keys j0 .. j0+63 (two 32-key halves)
-      floatx16 s[2];
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < HS / 16; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-              &Ks[buf][(kt * 32 + (lane & 31)) * KP + 16 * kk + 8 * hi]);
-          s[kt] = mfma32(kf, qf[kk], s[kt]);
-        }
-      }
-      // ---- scale, causal mask, tile max
-      const bool diag = (j0 + kAttnBK - 1 > q0);
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float t = s[kt][r] * scale_log2;
-          if (diag) {
-            const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key > myq) t = -INFINITY;
-          }
-          s[kt][r] = t;
-          tmax = fmaxf(tmax, t);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float m_new = fmaxf(m, tmax);  // finite: key 0 was seen first
-      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      float rs = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[kt][r] - m_new);
-          s[kt][r] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 32);
-      l = l * alpha + rs;
-      m = m_new;
-#pragma unroll
-      for (int dt = 0; dt < HS / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-
-      // ---- O^T += V^T P^T.  P^T operand: lane holds, for key group (kt, u),
-      // keys kt*32 + 16u + 8*(e/4) + 4*hi + e%4 of its query (e = 0..7).
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8 pf;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[e] = (__bf16)s[kt][8 * u + e];
-          const int kb = kt * 32 + 16 * u + 4 * hi;
-#pragma unroll
-          for (int dt = 0; dt < HS / 32; ++dt) {
-            const bf16_t* vrow = &Vt[buf][(dt * 32 + (lane & 31)) * VP + kb];
-            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-            const uint2 hi8 = *reinterpret_cast<const uint2*>(vrow + 8);
-            uint4 w;
-            w.x = lo.x; w.y = lo.y; w.z = hi8.x; w.w = hi8.y;
-            const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
-            acc[dt] = mfma32(vf, pf, acc[dt]);
-          }
-        }
-    }
-
-    if (it + 1 < nkv) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- normalise and write o into the merged-head layout
-  if (myq < T) {
-    const float inv = 1.f / l;
-    const int C = HS * H_;
-    bf16_t* orow = O + ((size_t)b * T + myq) * C + h * HS;
-#pragma unroll
-    for (int dt = 0; dt < HS / 32; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = dt * 32 + 8 * g + 4 * hi;
-        uint2 w;
-        w.x = pack_bf16x2(acc[dt][4 * g + 0] * inv, acc[dt][4 * g + 1] * inv);
-        w.y = pack_bf16x2(acc[dt][4 * g + 2] * inv, acc[dt][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d0) = w;
-      }
-    if (lse != nullptr && hi == 0)
-      lse[(size_t)bh * T + myq] = (m + __log2f(l)) * 0.69314718055994530942f;
-  }
-}
 
 // ----------------------------------------------------- bf16, pipelined
-// Second-generation bf16 kernel (the one the library launches).  Same wave
-// decomposition and S^T = K Q^T formulation as above, with:
+// Details of the bf16 kernel:
 //  * K and V tiles moved global -> LDS by global_load_lds_dwordx4 into an
 //    NS-stage ring (manual vmcnt waits, bare barriers), rows of hs elements
 //    with 16-byte chunks XOR-swizzled by the key row;
@@ -322,7 +120,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
   const int kv_end = min(T, (qt + 1) * kAttnBQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
 
-  auto issue = [&](int stage, int j0) {
+  // Loads of the K and V tile starting at key j0 into the ring stage at dst.
+  auto issue = [&](char* dst, int j0) {
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
       const int inst = wid * LPW + q;
@@ -334,7 +133,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
                             : reinterpret_cast<const bf16_t*>(&g_zero16);
       const bf16_t* gv = ok ? Vh + (size_t)key * HS + chunk * 8
                             : reinterpret_cast<const bf16_t*>(&g_zero16);
-      char* base = smem + stage * STAGE + inst * 1024;
+      char* base = dst + inst * 1024;
       __builtin_amdgcn_load_to_lds((void*)gk, GA_LDS(base), 16, 0, 0);
       __builtin_amdgcn_load_to_lds((void*)gv, GA_LDS(base + TILE), 16, 0, 0);
     }
@@ -342,19 +141,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
 
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nkv) issue(s, s * BKV);
+    if (s < nkv) issue(smem + s * STAGE, s * BKV);
 
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((address_space(3))) const bf16x8 lds_b128;
-  const lds_char* lbase = (const lds_char*)smem;
 
-  // One 64-key tile.  MASK: apply the causal mask (diagonal tiles).
-  auto tile = [&](auto mask_tag, int stage_off, int j0) {
+  // One 64-key tile held in ring stage rd; first issues the loads of the tile
+  // at key jn into stage wr (when jn >= 0).  MASK: apply the causal mask
+  // (diagonal tiles).  rd and wr are distinct stages: the restrict qualifiers
+  // tell the compiler so, and it then does not make the reads of rd wait for
+  // the loads into wr (the ring's vmcnt waits and barriers order them).
+  auto tile = [&](auto mask_tag, const char* __restrict__ rd, char* __restrict__ wr, int jn,
+                  int j0) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    if (jn >= 0) issue(wr, jn);
+    const lds_char* lbase = (const lds_char*)rd;
     // ---- S^T = K Q^T for keys j0 .. j0+63
     int ka[HS / 16];
 #pragma unroll
-    for (int kk = 0; kk < HS / 16; ++kk) ka[kk] = stage_off + koff[kk];
+    for (int kk = 0; kk < HS / 16; ++kk) ka[kk] = koff[kk];
     floatx16 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -415,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     // of the P registers: element e <-> key kb + 8(e/4) + 4*hi + e%4.
     int va[HS / 32];
 #pragma unroll
-    for (int dt = 0; dt < HS / 32; ++dt) va[dt] = stage_off + TILE + voff[dt];
+    for (int dt = 0; dt < HS / 32; ++dt) va[dt] = TILE + voff[dt];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -439,7 +244,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
       }
   };
 
-  // Ring step: wait for tile `it`, publish it, refill the ring.
+  // Ring step: wait for tile `it` and publish it; returns the first key of
+  // the tile whose loads refill the ring (-1: none left).
   auto step = [&](int it) {
     const int later = min(nkv - 1, it + NS - 2) - it;
     if (later >= NS - 2) wait_vmcnt<kLoads * (NS - 2)>();
@@ -447,21 +253,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     else if (later == 1) wait_vmcnt<kLoads>();
     else wait_vmcnt<0>();
     bar_nofence();
-    if (it + NS - 1 < nkv) issue((it + NS - 1) % NS, (it + NS - 1) * BKV);
+    return it + NS - 1 < nkv ? (it + NS - 1) * BKV : -1;
   };
   // Tiles wholly below the block's first query need no mask for any wave;
   // the last (at most two) tiles reach the diagonal.
   const int n_full = min(nkv, (qt * kAttnBQ) / BKV);
   int it = 0;
   for (; it < n_full; ++it) {
-    step(it);
-    tile(std::integral_constant<bool, false>{}, (it % NS) * STAGE, it * BKV);
+    const int jn = step(it);
+    tile(std::integral_constant<bool, false>{}, smem + (it % NS) * STAGE,
+         smem + ((it + NS - 1) % NS) * STAGE, jn, it * BKV);
   }
   for (; it < nkv; ++it) {
-    step(it);
+    const int jn = step(it);
     const int j0 = it * BKV;
+    char* wr = smem + ((it + NS - 1) % NS) * STAGE;
     if (j0 <= q0 + 31)  // skip tiles wholly in this wave's future
-      tile(std::integral_constant<bool, true>{}, (it % NS) * STAGE, j0);
+      tile(std::integral_constant<bool, true>{}, smem + (it % NS) * STAGE, wr, jn, j0);
+    else if (jn >= 0)
+      issue(wr, jn);
   }
 
   if (myq < T) {

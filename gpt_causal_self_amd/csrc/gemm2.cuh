@@ -233,15 +233,58 @@ struct Epi2Partial {
   }
 };
 
-template <int BM, int BN, int BK, int NSTAGE, bool A_KC, bool B_KC, int WGM, int WGN, class Epi>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(
+// One step of the ring: issue the loads of a later k-tile into stage `wr`
+// (when `load`) and multiply the k-tile held in stage `rd` into acc.  The two
+// stages are disjoint; the restrict qualifiers tell the compiler so, and it
+// then does not make the operand reads wait for the loads just issued (the
+// caller's vmcnt wait and barrier order each stage's loads before its reads).
+template <int BM, int BN, int BK, bool A_KC, bool B_KC, int WGM, int WGN>
+__device__ __forceinline__ void g2_step(const char* __restrict__ rd, char* __restrict__ wr,
+                                        bool load, const bf16_t* __restrict__ A, int lda,
+                                        const bf16_t* __restrict__ Bm, int ldb, int m0, int n0,
+                                        int M, int N, int kload, int kend, int wid, int lane,
+                                        int wm, int wn,
+                                        floatx16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MT = WTM / 32, NT = WTN / 32;
+  constexpr int kA = BM * BK * 2;
+  if (load) {
+    g2_issue<BM, BK, A_KC, NW>(A, lda, m0, M, kload, kend, wr, wid, lane);
+    g2_issue<BN, BK, B_KC, NW>(Bm, ldb, n0, N, kload, kend, wr + kA, wid, lane);
+  }
+#pragma unroll
+  for (int kk = 0; kk < BK / 16; ++kk) {
+    bf16x8 af[MT], bfr[NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) af[i] = g2_frag<BM, BK, A_KC>(rd, wm * WTM + i * 32, kk, lane);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) bfr[j] = g2_frag<BN, BK, B_KC>(rd + kA, wn * WTN + j * 32, kk, lane);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
+  }
+}
+
+// OCC: waves per SIMD the register allocation must allow (1 = no limit
+// beyond the block size).
+template <int BM, int BN, int BK, int NSTAGE, bool A_KC, bool B_KC, int WGM, int WGN, class Epi,
+          int OCC = 1>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(OCC)))
+void gemm2_kernel(
     const bf16_t* __restrict__ A, int lda, const bf16_t* __restrict__ Bm, int ldb, int M, int N,
     int K, int k_split, Epi epi) {
   constexpr int NW = WGM * WGN;
   using Cfg = Gemm2Cfg<BM, BN, BK, NSTAGE, A_KC, B_KC, NW>;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MT = WTM / 32, NT = WTN / 32;
-  __shared__ __align__(1024) char smem[Cfg::kSmem];
+  // A staging epilogue reuses the ring's LDS, grown to the output tile when
+  // that still fits the CU's 160 KB.
+  constexpr int kEpiBytes = Staged<Epi>::value ? BM * (BN + 8) * 2 : 0;
+  constexpr int kSmemAll =
+      kEpiBytes > Cfg::kSmem && kEpiBytes <= 160 * 1024 ? kEpiBytes : Cfg::kSmem;
+  __shared__ __align__(1024) char smem[kSmemAll];
 
   const int tiles_n = (N + BN - 1) / BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -251,12 +294,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(
   const int kbeg = (int)blockIdx.y * k_split;
   const int kend = min(K, kbeg + k_split);
   const int nk = (kend - kbeg + BK - 1) / BK;
-
-  auto issue = [&](int stage, int kt) {
-    char* sa = smem + stage * Cfg::kStage;
-    g2_issue<BM, BK, A_KC, NW>(A, lda, m0, M, kbeg + kt * BK, kend, sa, wid, lane);
-    g2_issue<BN, BK, B_KC, NW>(Bm, ldb, n0, N, kbeg + kt * BK, kend, sa + Cfg::kA, wid, lane);
-  };
 
   floatx16 acc[MT][NT];
 #pragma unroll
@@ -268,7 +305,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(
 
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < nk) issue(s, s);
+    if (s < nk) {
+      char* sa = smem + s * Cfg::kStage;
+      g2_issue<BM, BK, A_KC, NW>(A, lda, m0, M, kbeg + s * BK, kend, sa, wid, lane);
+      g2_issue<BN, BK, B_KC, NW>(Bm, ldb, n0, N, kbeg + s * BK, kend, sa + Cfg::kA, wid, lane);
+    }
 
   for (int kt = 0; kt < nk; ++kt) {
     // tile kt is complete once at most (later tiles issued) x loads remain
@@ -278,24 +319,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(
     else if (later == 1) wait_vmcnt<Cfg::kLoads>();
     else wait_vmcnt<0>();
     bar_nofence();
-    if (kt + NSTAGE - 1 < nk) issue((kt + NSTAGE - 1) % NSTAGE, kt + NSTAGE - 1);
-    const char* sa = smem + (kt % NSTAGE) * Cfg::kStage;
-    const char* sb = sa + Cfg::kA;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[MT], bfr[NT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) af[i] = g2_frag<BM, BK, A_KC>(sa, wm * WTM + i * 32, kk, lane);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) bfr[j] = g2_frag<BN, BK, B_KC>(sb, wn * WTN + j * 32, kk, lane);
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
-    }
+    const int kn = kt + NSTAGE - 1;
+    g2_step<BM, BN, BK, A_KC, B_KC, WGM, WGN>(
+        smem + (kt % NSTAGE) * Cfg::kStage, smem + (kn % NSTAGE) * Cfg::kStage, kn < nk, A, lda,
+        Bm, ldb, m0, n0, M, N, kbeg + kn * BK, kend, wid, lane, wm, wn, acc);
   }
 
-  if constexpr (Staged<Epi>::value && BM * (BN + 8) * 2 <= Cfg::kSmem) {
+  if constexpr (Staged<Epi>::value && BM * (BN + 8) * 2 <= kSmemAll) {
     // ---- staged epilogue: bias + bf16 rounding into an LDS tile [BM][BN+8],
     // then every 8 lanes store one 128-byte run of a row.
     constexpr int SP = BN + 8;  // pitch (elements); 16-byte aligned rows
@@ -366,7 +396,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm2_kernel(
 
 // splits > 1 divides K into that many slices (multiples of BK); returns the
 // number of slices launched.
-template <int BM, int BN, int NSTAGE, int BK, int WGM, int WGN, bool A_KC, bool B_KC, class Epi>
+template <int BM, int BN, int NSTAGE, int BK, int WGM, int WGN, bool A_KC, bool B_KC,
+          int OCC = 1, class Epi>
 inline int launch_gemm2(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N,
                         int K, const Epi& epi, hipStream_t st, int splits = 1) {
   const int grid = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
@@ -375,7 +406,7 @@ inline int launch_gemm2(const bf16_t* A, int lda, const bf16_t* B, int ldb, int 
   int k_split = (K + splits - 1) / splits;
   k_split = (k_split + BK - 1) / BK * BK;
   const int ns = (K + k_split - 1) / k_split;
-  hipLaunchKernelGGL((gemm2_kernel<BM, BN, BK, NSTAGE, A_KC, B_KC, WGM, WGN, Epi>),
+  hipLaunchKernelGGL((gemm2_kernel<BM, BN, BK, NSTAGE, A_KC, B_KC, WGM, WGN, Epi, OCC>),
                      dim3(grid, ns), dim3(64 * WGM * WGN), 0, st, A, lda, B, ldb, M, N, K,
                      k_split, epi);
   return ns;
