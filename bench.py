@@ -13,6 +13,13 @@ bf16 MFMA peak, per-kernel times from HIP events recorded by the library on
 the launch stream, the roofline of the dominant kernel, the training step
 (forward + backward) time of the same workload, and the CPU oracle timed on a
 bounded sample of the same workload on the host cores.
+
+HBM traffic of the dominant kernel comes from two rocprofv3 counter passes
+over `--pmc-run` (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same
+counter reads for a plain device copy of known size launched in the same
+run; `--write-traffic FETCH_DIR WRITE_DIR` turns the two passes into the
+summary under profiles/, which the benchmark reports while the kernel sources
+it was taken from are unchanged (else null).
 """
 from __future__ import annotations
 
@@ -32,6 +39,10 @@ PEAK_HBM_GBS = 8000.0
 METRIC = ("attention-layer TFLOP/s + tokens/s at B=12,T=1024,C=768,H=12 bf16; "
           "% of MFMA peak")
 N_SETS = 8
+COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_kernels_gpt2_124m_B12_T1024.md")
+KERNEL_KEYS = {"c_attn": ("gemm2_kernel", "Epi2QKV"), "attention": ("attn_fwd2_bf16_kernel",),
+               "c_proj": ("gemm2_kernel", "Epi2RowMajor")}
 
 
 def layer_flops(B, T, C):
@@ -85,23 +96,184 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def cpu_baseline(workload_index, n_seq):
+def cpu_baseline(workload_index, n_seq, min_seconds=10.0):
     """The fp64 oracle, as it stands, on the first n_seq sequences of the
-    same workload (sequences are independent, so throughput scales)."""
+    same workload (sequences are independent, so throughput scales), run
+    repeatedly until about min_seconds of CPU time have elapsed."""
     import oracle
     from gpt_causal_self_amd.inputs import workload_inputs
     inp = workload_inputs(workload_index, B=n_seq)
     threads = oracle.default_threads()
     oracle.load()
-    t0 = time.perf_counter()
-    oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.n_head,
-                   nthreads=threads)
-    dt = time.perf_counter() - t0
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.n_head,
+                       nthreads=threads)
+        runs += 1
+        if time.perf_counter() - t0 >= min_seconds or runs >= 50:
+            break
+    dt = (time.perf_counter() - t0) / runs
     B, T, C = inp.x.shape
     return {"value": layer_flops(B, T, C) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "tokens_per_s": B * T / dt, "seconds": dt,
-            "sample": f"{n_seq} of 12 sequences (B={n_seq}, T=1024, C=768, H=12), "
-                      "fp64 forward, same seeded inputs"}
+            "kind": "oracle", "tokens_per_s": B * T / dt, "seconds_per_run": dt, "runs": runs,
+            "sample": f"{n_seq} of 12 sequences (B={n_seq}, T=1024, C=768, H=12), fp64 "
+                      f"forward on the same seeded inputs, mean of {runs} runs"}
+
+
+def sources_digest():
+    """sha256 over the HIP sources and header the kernels are built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for d in (os.path.join(ROOT, "gpt_causal_self_amd", "csrc"), os.path.join(ROOT, "include")):
+        for f in sorted(os.listdir(d)):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def _counter_means(run_dir, counter):
+    """Mean per-dispatch value of one counter, per kernel group and for the
+    calibration copy, from a rocprofv3 -f csv output directory."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    sums, counts = {}, {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"]
+            key = None
+            for k, parts in KERNEL_KEYS.items():
+                if all(p in name for p in parts):
+                    key = k
+            if key is None and "copybuffer" in name.lower():
+                key = "copy"
+            if key is None:
+                continue
+            d = r.get("Dispatch_Id", r.get("Correlation_Id"))
+            sums.setdefault(key, {}).setdefault(d, 0.0)
+            sums[key][d] += float(r["Counter_Value"])
+    out = {}
+    for k, per in sums.items():
+        vals = list(per.values())
+        if k == "copy":
+            vals = [max(vals)]            # the 1 GiB calibration copy
+        out[k] = sum(vals) / len(vals)
+    return out
+
+
+def write_traffic(fetch_dir, write_dir):
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    ff = COPY_BYTES / 1024.0 / fetch["copy"]
+    fw = COPY_BYTES / 1024.0 / write["copy"]
+    from gpt_causal_self_amd.inputs import WORKLOADS
+    w = WORKLOADS[2]
+    sb = stage_bytes(w.B, w.T, w.C, w.H)
+    rec = {"digest": sources_digest(), "factor_fetch": ff, "factor_write": fw,
+           "copy_fetch_kib": fetch["copy"], "copy_write_kib": write["copy"], "kernels": {}}
+    lines = ["# HBM traffic per launch: GPT-2 124M attention layer forward "
+             "(B12 T1024 C768 H12 bf16)", "",
+             "Commands (from /tmp with TMPDIR=/tmp on one MI355X; repository at $R):", "", "```",
+             "timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pmc_fetch "
+             "-- python3 $R/bench.py --pmc-run",
+             "timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pmc_write "
+             "-- python3 $R/bench.py --pmc-run",
+             "python3 $R/bench.py --write-traffic $R/gpurun_out/pmc_fetch $R/gpurun_out/pmc_write",
+             "```", "",
+             f"Calibration: a device copy of {COPY_BYTES} bytes reads FETCH_SIZE "
+             f"{fetch['copy']:.1f} KiB and WRITE_SIZE {write['copy']:.1f} KiB, so each kernel's "
+             f"counters are scaled by {ff:.4f} (reads) and {fw:.4f} (writes).", "",
+             "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled MB read | scaled MB written | "
+             "algorithmic MB | traffic / algorithmic |", "|---|---|---|---|---|---|---|"]
+    for k in ("c_attn", "attention", "c_proj"):
+        if k not in fetch or k not in write:
+            continue
+        rb, wb = fetch[k] * 1024 * ff, write[k] * 1024 * fw
+        rec["kernels"][k] = {"fetch_kib": fetch[k], "write_kib": write[k],
+                             "bytes": rb + wb, "algorithmic_bytes": sb[k]}
+        lines.append(f"| {k} | {fetch[k]:.1f} | {write[k]:.1f} | {rb / 1e6:.2f} | "
+                     f"{wb / 1e6:.2f} | {sb[k] / 1e6:.2f} | {(rb + wb) / sb[k]:.3f} |")
+    lines += ["", "Machine-readable record (sources digest = sha256 of the HIP sources and "
+              "header the counters were taken with):", "", "```",
+              "TRAFFIC " + json.dumps(rec, sort_keys=True), "```", ""]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def write_kernel_stats(stats_dir, out_md):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(stats_dir, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {stats_dir}")
+    rows = list(csv.DictReader(open(files[0])))
+
+    def short(n):
+        n = re.sub(r"\(.*", "", n)
+        return n.replace("void gpt_attn::", "").replace("unsigned short", "bf16")
+    lines = ["# Kernel trace: GPT-2 124M attention layer (B12 T1024 C768 H12 bf16), "
+             "bench.py forward + training step", "",
+             "Command (from /tmp with TMPDIR=/tmp on one MI355X; repository at $R):", "", "```",
+             "timeout -k 10 300 rocprofv3 --kernel-trace --stats -f csv -d "
+             "$R/gpurun_out/ktrace -o run -- python3 $R/bench.py --steps 20 --warmup 5 --no-cpu",
+             f"python3 $R/bench.py --write-kernel-stats $R/gpurun_out/ktrace {os.path.basename(out_md)}",
+             "```", "", f"Sources digest: {sources_digest()}", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    with open(os.path.join(ROOT, "profiles", os.path.basename(out_md)), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def load_traffic():
+    """The counter-derived traffic record, or None if absent or taken with
+    other kernel sources."""
+    try:
+        for line in open(TRAFFIC_FILE):
+            if line.startswith("TRAFFIC "):
+                rec = json.loads(line[len("TRAFFIC "):])
+                return rec if rec.get("digest") == sources_digest() else None
+    except OSError:
+        pass
+    return None
+
+
+def pmc_run(steps):
+    """Short run for the counter passes: forward steps of the workload, then
+    the calibration copy."""
+    import torch
+    from gpt_causal_self_amd import gpt_attn as ga
+    from gpt_causal_self_amd.inputs import WORKLOADS, make_inputs, to_torch
+    w = WORKLOADS[2]
+    B, T, C, H = w.B, w.T, w.C, w.H
+    dev = torch.device("cuda", 0)
+    inp = make_inputs(B, T, C, H, bias=True, dtype="bf16", seed=125, w_std=w.w_std,
+                      b_attn_std=w.b_attn_std, proj_std=w.proj_std, b_proj_std=w.b_proj_std)
+    t = {k: to_torch(getattr(inp, k), "bf16", dev)
+         for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj")}
+    y = torch.empty_like(t["x"])
+    layer = ga.Layer(C, H, B, T, "bf16")
+    for _ in range(steps):
+        ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"], t["W_proj"],
+                            t["b_proj"], H, y)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    layer.close()
+    print(f"pmc run: {steps} forward steps, copy of {COPY_BYTES} bytes", flush=True)
 
 
 def main():
@@ -112,12 +284,28 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-train", action="store_true", help="skip the fwd+bwd measurement")
     ap.add_argument("--cpu-seqs", type=int, default=12)
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="short forward-only run plus the calibration copy, for counter passes")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 counter passes into the traffic record")
+    ap.add_argument("--write-kernel-stats", nargs=2, metavar=("STATS_DIR", "NAME"),
+                    help="summarise a rocprofv3 --kernel-trace --stats run under profiles/")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
+    if args.write_kernel_stats:
+        write_kernel_stats(*args.write_kernel_stats)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the layer runs on a single device; see the sharding notes in DESIGN.md)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_run:
+        pmc_run(min(args.steps, 10))
+        return
 
     import torch
     from gpt_causal_self_amd import gpt_attn as ga
@@ -186,9 +374,16 @@ def main():
                       "flop_per_launch": sf[k], "bytes_per_launch": sb[k]}
     dom = max(("c_attn", "attention", "c_proj"), key=lambda k: mean[k])
     achieved = sf[dom] / (mean[dom] * 1e-3) / 1e12
+    rec = load_traffic()
+    traffic = None
+    if rec and dom in rec["kernels"]:
+        traffic = round(rec["kernels"][dom]["bytes"])
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                "copy-calibrated)" if traffic else None,
+                "algorithmic_bytes": sb[dom], "flop_per_launch": sf[dom]}
 
     out = {"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),

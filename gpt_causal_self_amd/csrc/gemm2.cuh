@@ -288,7 +288,14 @@ void gemm2_kernel(
 
   const int tiles_n = (N + BN - 1) / BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int m0 = (tile / tiles_n) * BM, n0 = (tile % tiles_n) * BN;
+  // Each XCD's run of consecutive tiles covers a band of row tiles; within
+  // a band the order is column-major, so a band's A rows stay in that XCD's
+  // L2 while the B columns stream through once.
+  const int tiles_m = (M + BM - 1) / BM;
+  const int band = max(1, tiles_m / 8);
+  const int bi = tile / (band * tiles_n), loc = tile - bi * band * tiles_n;
+  const int rows = min(band, tiles_m - bi * band);
+  const int m0 = (bi * band + loc % rows) * BM, n0 = (loc / rows) * BN;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
   const int kbeg = (int)blockIdx.y * k_split;
