@@ -276,6 +276,76 @@ def pmc_run(steps):
     print(f"pmc run: {steps} forward steps, copy of {COPY_BYTES} bytes", flush=True)
 
 
+def time_calls(fn, n, warm=3):
+    """Mean milliseconds per call of fn (launches on the current stream),
+    from torch events around n back-to-back calls."""
+    import torch
+    for _ in range(warm):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(n):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def next_rows(n=50):
+    """Timings of the Block pieces at the GPT-2 124M shape (B=12, T=1024,
+    C=768, 12 heads, MLP width 3072): LayerNorm, the Pre-LN attention
+    half-block and the MLP sublayer with its residual add."""
+    import torch
+    from gpt_causal_self_amd import gpt_attn as ga
+    from gpt_causal_self_amd.inputs import (WORKLOADS, make_inputs, make_ln_params,
+                                            make_mlp_inputs, to_torch)
+    w = WORKLOADS[2]
+    B, T, C, H = w.B, w.T, w.C, w.H
+    M, F = B * T, 4 * C
+    dev = "cuda"
+    inp = make_inputs(B, T, C, H, bias=True, dtype="bf16", seed=125, w_std=w.w_std,
+                      b_attn_std=w.b_attn_std, proj_std=w.proj_std, b_proj_std=w.b_proj_std)
+    t = {k: to_torch(getattr(inp, k), "bf16", dev)
+         for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj")}
+    lw, lb = (to_torch(a, "bf16", dev) for a in make_ln_params(C, seed=126))
+    out = torch.empty_like(t["x"])
+    layer = ga.Layer(C, H, B, T, "bf16")
+    res = {}
+    ms = time_calls(lambda: ga.gpt_layernorm(t["x"], lw, lb, out), n)
+    ln_bytes = 2 * M * C * 2 + 2 * C * 2
+    res["layernorm"] = {"workload": f"M={M} C={C} bf16", "ms": round(ms, 5),
+                        "gbs": round(ln_bytes / (ms * 1e-3) / 1e9, 1),
+                        "roofline": {"bound": "hbm", "achieved": round(ln_bytes / (ms * 1e-3) / 1e9, 1),
+                                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                     "frac": round(ln_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                     "algorithmic_bytes": ln_bytes}}
+    ms = time_calls(lambda: ga.gpt_attn_block_forward(layer.h, t["x"], lw, lb, t["W_attn"],
+                                                      t["b_attn"], t["W_proj"], t["b_proj"], H,
+                                                      out), n)
+    F_blk = layer_flops(B, T, C)
+    res["block_attn_half"] = {"workload": f"x + attn(ln_1(x)), B={B} T={T} C={C} H={H} bf16",
+                              "ms": round(ms, 5),
+                              "tflops": round(F_blk / (ms * 1e-3) / 1e12, 2),
+                              "tokens_per_s": round(M / (ms * 1e-3), 1)}
+    layer.close()
+    m = make_mlp_inputs(M, C, F, seed=127, with_residual=True)
+    d = {k: to_torch(getattr(m, k), "bf16", dev)
+         for k in ("x", "W_fc", "b_fc", "W_proj", "b_proj", "residual")}
+    hbuf = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((M, C), dtype=torch.bfloat16, device=dev)
+    ms = time_calls(lambda: ga.gpt_mlp_forward(d["x"], d["W_fc"], d["b_fc"], d["W_proj"],
+                                               d["b_proj"], hbuf, y, residual=d["residual"]), n)
+    F_mlp = 4 * M * C * F
+    res["mlp"] = {"workload": f"x + mlp(x), M={M} C={C} F={F} bf16", "ms": round(ms, 5),
+                  "tflops": round(F_mlp / (ms * 1e-3) / 1e12, 2),
+                  "roofline": {"bound": "mfma", "achieved": round(F_mlp / (ms * 1e-3) / 1e12, 2),
+                               "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(F_mlp / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                               "flop_per_launch": F_mlp}}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +354,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-train", action="store_true", help="skip the fwd+bwd measurement")
     ap.add_argument("--cpu-seqs", type=int, default=12)
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the Block-piece timings (LayerNorm, half-block, MLP)")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short forward-only run plus the calibration copy, for counter passes")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -430,6 +502,9 @@ def main():
                                  "flop_count": "3 x forward causal count"}
         except ga.GptAttnError as e:
             out["train_step"] = {"error": str(e)}
+
+    if not args.no_next:
+        out["next_rows"] = next_rows()
 
     if not args.no_cpu:
         cb = cpu_baseline(2, args.cpu_seqs)

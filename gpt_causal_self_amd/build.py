@@ -1,7 +1,9 @@
 """Build the HIP library ``libgpt_attn.so`` in-tree with hipcc for gfx950.
 
-One translation unit (``csrc/gpt_attn.hip``) holds the C ABI and includes the
-kernel headers.  Packed-fp32 instructions are disabled for every kernel
+Two translation units hold the C ABI and include the kernel headers:
+``csrc/gpt_attn.hip`` (the attention layer, include/gpt_attn.h) and
+``csrc/gpt_block.hip`` (LayerNorm, the Pre-LN half-block, the MLP;
+include/gpt_block.h).  Packed-fp32 instructions are disabled for every kernel
 (``-target-feature -packed-fp32-ops``); hipcc's host pass warns that it does
 not know that feature, which is harmless.
 """
@@ -14,7 +16,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "gpt_attn.hip")
+SRCS = [os.path.join(HERE, "csrc", "gpt_attn.hip"), os.path.join(HERE, "csrc", "gpt_block.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgpt_attn.so")
 ARCH = os.environ.get("GPT_ATTN_ARCH", "gfx950")
@@ -31,7 +33,7 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wno-unused-command-line-argument", "-I", INCLUDE, *extra, SRC, "-o", tmp]
+           "-Wno-unused-command-line-argument", "-I", INCLUDE, *extra, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -211,6 +211,45 @@ struct Epi2QKV {
   }
 };
 
+// Exact GELU, g(v) = v * Phi(v) = v/2 * (1 + erf(v / sqrt(2))) (page "nanoGPT
+// architecture explained step by step", section 4).
+__device__ __forceinline__ float gelu_erf(float v) {
+  return 0.5f * v * (1.f + erff(v * 0.70710678118654752f));
+}
+
+// MLP c_fc epilogue: bias, exact GELU, rounding; row-major [M][ldc].
+struct Epi2Gelu {
+  bf16_t* out;
+  int ldc;
+  const bf16_t* bias;  // may be NULL
+  static constexpr int kAct = 1;
+  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
+    float b[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+      const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
+      b[0] = bf2f(u.x & 0xffff); b[1] = bf2f(u.x >> 16);
+      b[2] = bf2f(u.y & 0xffff); b[3] = bf2f(u.y >> 16);
+    }
+    uint2 w;
+    w.x = pack_bf16x2(gelu_erf(v[0] + b[0]), gelu_erf(v[1] + b[1]));
+    w.y = pack_bf16x2(gelu_erf(v[2] + b[2]), gelu_erf(v[3] + b[3]));
+    *reinterpret_cast<uint2*>(out + (size_t)m * ldc + n) = w;
+  }
+  static constexpr bool kStaged = true;
+  __device__ __forceinline__ float bias_at(int n) const { return bias ? bf2f(bias[n]) : 0.f; }
+  __device__ __forceinline__ void store8(int m, int n, uint4 w) const {
+    *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = w;
+  }
+};
+
+// Activation applied after the bias in the staged epilogue (0: none).
+template <class Epi, class = void>
+struct ActOf { static constexpr int value = 0; };
+template <class Epi>
+struct ActOf<Epi, decltype(void(Epi::kAct))> { static constexpr int value = Epi::kAct; };
+template <int ACT>
+__device__ __forceinline__ float apply_act(float v) { return ACT == 1 ? gelu_erf(v) : v; }
+
 template <class Epi, class = void>
 struct Staged { static constexpr bool value = false; };
 template <class Epi>
@@ -351,8 +390,11 @@ void gemm2_kernel(
         for (int i = 0; i < MT; ++i) {
           const int rl = wm * WTM + i * 32 + (lane & 31);
           uint2 w;
-          w.x = pack_bf16x2(acc[i][j][4 * g] + b[0], acc[i][j][4 * g + 1] + b[1]);
-          w.y = pack_bf16x2(acc[i][j][4 * g + 2] + b[2], acc[i][j][4 * g + 3] + b[3]);
+          constexpr int ACT = ActOf<Epi>::value;
+          w.x = pack_bf16x2(apply_act<ACT>(acc[i][j][4 * g] + b[0]),
+                            apply_act<ACT>(acc[i][j][4 * g + 1] + b[1]));
+          w.y = pack_bf16x2(apply_act<ACT>(acc[i][j][4 * g + 2] + b[2]),
+                            apply_act<ACT>(acc[i][j][4 * g + 3] + b[3]));
           *reinterpret_cast<uint2*>(ct + rl * SP + cl) = w;
         }
       }

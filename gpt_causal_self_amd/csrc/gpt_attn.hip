@@ -6,114 +6,11 @@
 //             -> fused causal attention (merged-head output, optional LSE)
 //             -> c_proj GEMM (bias)
 //   backward: see attn_bwd.cuh / the launch sequence in gpt_attn_backward.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-#include <stdlib.h>
-#include <math.h>
-
-#include "../../include/gpt_attn.h"
 #include "attn_bwd.cuh"
-#include "attn_fwd.cuh"
-#include "gemm.cuh"
-#include "gemm2.cuh"
-
-// Tile shapes (BM, BN, pipeline stages, BK, wave grid rows, wave grid columns)
-// of the bf16 GEMMs.
-#ifndef GA_QKV_TILE
-#define GA_QKV_TILE 256, 256, 2, 64, 2, 4
-#endif
-#ifndef GA_PROJ_TILE
-#define GA_PROJ_TILE 192, 256, 2, 64, 2, 4
-#endif
-#ifndef GA_DGRAD_TILE
-#define GA_DGRAD_TILE 192, 256, 2, 64, 2, 4
-#endif
-#ifndef GA_ATTN_STAGES
-#define GA_ATTN_STAGES 2
-#endif
-#ifndef GA_WGRAD_TILE
-#define GA_WGRAD_TILE 128, 128, 2, 64, 2, 2
-#endif
+#include "handle.cuh"
+#include "layer_fwd.cuh"
 
 using namespace gpt_attn;
-
-struct gpt_attn_handle {
-  int C, H, hs, max_B, max_T, dtype;
-  int device;
-  size_t esize;  // bytes per element
-  char* ws;      // one allocation, carved below
-  size_t ws_bytes;
-  // carved regions
-  void* qkv;     // [3][B][H][T][hs]
-  void* o;       // [B][T][C]
-  float* lse;    // [B][H][T]
-  void* dym;     // [B][T][C]     backward: gradient of merged heads
-  void* dqkv;    // [B][T][3C]    backward: gradient of c_attn output
-  float* delta;  // [B][H][T]     backward: rowsum(dO * O)
-  float* part;   // split-K partial sums of weight gradients (fp32)
-  size_t part_elems;
-  // state of the last forward
-  int saved, saved_B, saved_T;
-  // optional stage events (measurement hook)
-  hipEvent_t ev[8];
-  int n_ev;
-};
-
-namespace {
-
-constexpr size_t kAlign = 256;
-inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
-
-// Upper bound on the split-K slices of the weight-gradient GEMMs, and the
-// number of row slices of the bias-gradient column sums.
-constexpr int kWgradSplits = 8;
-constexpr int kColsumSplits = 64;
-
-int check_dims(int C, int n_head, int max_B, int max_T, int dtype) {
-  if (C <= 0 || n_head <= 0 || max_B <= 0 || max_T <= 0) return GPT_ATTN_ERR_INVALID_ARG;
-  if (dtype != GPT_ATTN_F32 && dtype != GPT_ATTN_BF16) return GPT_ATTN_ERR_INVALID_ARG;
-  if (C % n_head != 0) return GPT_ATTN_ERR_SHAPE;
-  const int hs = C / n_head;
-  if (hs != 32 && hs != 64) return GPT_ATTN_ERR_UNSUPPORTED;
-  // every index below fits in 32 bits per tensor row count / 64-bit offsets
-  if ((long long)max_B * max_T > (1LL << 30)) return GPT_ATTN_ERR_SHAPE;
-  return GPT_ATTN_OK;
-}
-
-struct Layout {
-  size_t qkv, o, lse, dym, dqkv, delta, part, total, part_elems;
-};
-
-Layout layout(int C, int H, int max_B, int max_T, size_t es) {
-  Layout L;
-  const size_t BT = (size_t)max_B * max_T;
-  size_t off = 0;
-  L.qkv = off;   off = align_up(off + 3 * BT * C * es);
-  L.o = off;     off = align_up(off + BT * C * es);
-  L.lse = off;   off = align_up(off + (size_t)max_B * H * max_T * sizeof(float));
-  L.dym = off;   off = align_up(off + BT * C * es);
-  L.dqkv = off;  off = align_up(off + 3 * BT * C * es);
-  L.delta = off; off = align_up(off + (size_t)max_B * H * max_T * sizeof(float));
-  L.part_elems = (size_t)kWgradSplits * C * 3 * C + (size_t)kColsumSplits * 3 * C;
-  L.part = off;  off = align_up(off + L.part_elems * sizeof(float));
-  L.total = off;
-  return L;
-}
-
-inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
-
-inline void mark(const gpt_attn_handle* h, int i, hipStream_t st) {
-  if (i < h->n_ev) (void)hipEventRecord(h->ev[i], st);
-}
-
-inline int launch_status() {
-  const hipError_t e = hipGetLastError();
-  return e == hipSuccess ? GPT_ATTN_OK : GPT_ATTN_ERR_HIP;
-}
-
-}  // namespace
 
 extern "C" {
 
@@ -176,6 +73,7 @@ int gpt_attn_create(gpt_attn_t* out, int C, int n_head, int max_B, int max_T, in
   h->delta = (float*)(h->ws + L.delta);
   h->part = (float*)(h->ws + L.part);
   h->part_elems = L.part_elems;
+  h->ln = h->ws + L.ln;
   *out = h;
   return GPT_ATTN_OK;
 }
@@ -247,27 +145,12 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
   const size_t head_elems = (size_t)B * H * T * hs;  // one of q, k, v
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hs));
   float* lse = save_for_backward ? h->lse : nullptr;
+  (void)M;
 
   if (h->dtype == GPT_ATTN_BF16) {
-    const bf16_t* xb = (const bf16_t*)x;
-    bf16_t* qkv = (bf16_t*)h->qkv;
-    bf16_t* o = (bf16_t*)h->o;
-    Epi2QKV e1{qkv, (const bf16_t*)b_attn, B, T, C, H, hs};
-    mark(h, 0, st);
-    launch_gemm2<GA_QKV_TILE, true, false>(xb, C, (const bf16_t*)W_attn, 3 * C, M, 3 * C, C, e1,
-                                           st);
-    mark(h, 1, st);
-    const dim3 agrid(B * H, (T + kAttnBQ - 1) / kAttnBQ);
-    if (hs == 64)
-      hipLaunchKernelGGL((attn_fwd2_bf16_kernel<64, GA_ATTN_STAGES>), agrid, dim3(256), 0, st,
-                         qkv, qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
-    else
-      hipLaunchKernelGGL((attn_fwd2_bf16_kernel<32, GA_ATTN_STAGES>), agrid, dim3(256), 0, st,
-                         qkv, qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
-    mark(h, 2, st);
-    Epi2RowMajor e3{(bf16_t*)y, C, (const bf16_t*)b_proj};
-    launch_gemm2<GA_PROJ_TILE, true, false>(o, C, (const bf16_t*)W_proj, C, M, C, C, e3, st);
-    mark(h, 3, st);
+    layer_forward_bf16(h, (const bf16_t*)x, B, T, (const bf16_t*)W_attn, (const bf16_t*)b_attn,
+                       (const bf16_t*)W_proj, (const bf16_t*)b_proj, (bf16_t*)y, nullptr, lse,
+                       st);
   } else {
     const float* xf = (const float*)x;
     float* qkv = (float*)h->qkv;

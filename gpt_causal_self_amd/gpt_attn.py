@@ -1,4 +1,5 @@
-"""Thin ctypes binding of ``libgpt_attn.so`` (C ABI in ``include/gpt_attn.h``).
+"""Thin ctypes binding of ``libgpt_attn.so`` (C ABI in ``include/gpt_attn.h``
+and ``include/gpt_block.h``).
 
 Argument marshalling only: torch tensors supply device memory and
 ``torch.cuda.current_stream()`` supplies the stream; every step of the layer
@@ -20,7 +21,8 @@ F32, BF16 = 0, 1
 EXPORTED = ("gpt_attn_workspace_bytes", "gpt_attn_create", "gpt_attn_forward",
             "gpt_attn_backward", "gpt_attn_destroy", "gpt_attn_strerror",
             "gpt_attn_debug_workspace", "gpt_attn_set_stage_events",
-            "gpt_attn_debug_backward")
+            "gpt_attn_debug_backward", "gpt_layernorm", "gpt_attn_block_forward",
+            "gpt_mlp_forward")
 
 _lib = None
 
@@ -53,6 +55,9 @@ def lib():
                                                ctypes.POINTER(vp)]
         L.gpt_attn_debug_backward.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                               ctypes.POINTER(vp)]
+        L.gpt_layernorm.argtypes = [vp, i, i, vp, vp, vp, vp]
+        L.gpt_attn_block_forward.argtypes = [vp, vp, i, i, vp, vp, vp, vp, vp, vp, i, vp, vp]
+        L.gpt_mlp_forward.argtypes = [vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
         for name in EXPORTED:
             if name != "gpt_attn_strerror":
                 getattr(L, name).restype = i
@@ -149,6 +154,40 @@ def gpt_attn_debug_backward(h):
     _check(lib().gpt_attn_debug_backward(h, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)),
            "gpt_attn_debug_backward")
     return a.value, b.value, c.value
+
+
+def gpt_layernorm(x, w, b, out, stream=None, M=None, C=None):
+    """out = LayerNorm(x) over the last dimension (bf16 tensors)."""
+    if M is None or C is None:
+        C = int(x.shape[-1])
+        M = int(x.numel() // C) if C else 0
+    _check(lib().gpt_layernorm(_ptr(x), M, C, _ptr(w), _ptr(b), _ptr(out), _stream(stream)),
+           "gpt_layernorm")
+
+
+def gpt_attn_block_forward(h, x, ln_w, ln_b, W_attn, b_attn, W_proj, b_proj, n_head, out,
+                           stream=None, B=None, T=None):
+    """out = x + attn(ln_1(x)) on a bf16 handle."""
+    if B is None or T is None:
+        B, T = int(x.shape[0]), int(x.shape[1])
+    rc = lib().gpt_attn_block_forward(h, _ptr(x), B, T, _ptr(ln_w), _ptr(ln_b), _ptr(W_attn),
+                                      _ptr(b_attn), _ptr(W_proj), _ptr(b_proj), n_head,
+                                      _ptr(out), _stream(stream))
+    _check(rc, "gpt_attn_block_forward")
+
+
+def gpt_mlp_forward(x, W_fc, b_fc, W_proj, b_proj, hbuf, y, residual=None, stream=None,
+                    M=None, C=None, F=None):
+    """y = gelu(x W_fc + b_fc) W_proj + b_proj (+ residual); hbuf receives the
+    activations (bf16 tensors)."""
+    if M is None or C is None or F is None:
+        C = int(x.shape[-1])
+        M = int(x.numel() // C) if C else 0
+        F = int(W_fc.shape[-1])
+    rc = lib().gpt_mlp_forward(_ptr(x), M, C, F, _ptr(W_fc), _ptr(b_fc), _ptr(W_proj),
+                               _ptr(b_proj), _ptr(residual), _ptr(hbuf), _ptr(y),
+                               _stream(stream))
+    _check(rc, "gpt_mlp_forward")
 
 
 class Layer:

@@ -164,6 +164,48 @@ def workload_inputs(index: int, *, B=None, T=None, with_dY=None) -> LayerInputs:
     return inp
 
 
+def make_ln_params(C, *, seed, dtype="bf16", w_std=0.1, b_std=0.1, bias=True):
+    """LayerNorm weight and bias.  GPT-2 initialises them to 1 and 0; the
+    tests draw them around that point (1 + N(0, w_std), N(0, b_std)) so that
+    a swapped or dropped scale or shift is visible."""
+    rng = np.random.default_rng(seed)
+    w = 1.0 + rng.standard_normal(C, dtype=np.float32) * np.float32(w_std)
+    b = rng.standard_normal(C, dtype=np.float32) * np.float32(b_std) if bias else None
+    return to_dtype(w, dtype), None if b is None else to_dtype(b, dtype)
+
+
+@dataclasses.dataclass
+class MlpInputs:
+    x: np.ndarray            # [M, C]
+    W_fc: np.ndarray         # [C, F]
+    b_fc: np.ndarray | None  # [F]
+    W_proj: np.ndarray       # [F, C]
+    b_proj: np.ndarray | None
+    residual: np.ndarray | None
+
+
+def make_mlp_inputs(M, C, F, *, seed, dtype="bf16", bias=True, with_residual=False,
+                    w_std=0.02, proj_std=0.02 / math.sqrt(24), b_std=0.02):
+    """MLP sublayer inputs: x ~ N(0, 1) standing in for ln_2(x); c_fc weights
+    N(0, 0.02) and the residual projection N(0, 0.02 / sqrt(2 n_layer)) as the
+    pages' initialisation (n_layer = 12 by default); draw order x, W_fc, b_fc,
+    W_proj, b_proj, residual."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+
+    def normal(shape, std):
+        return rng.standard_normal(shape, dtype=np.float32) * f32(std)
+
+    x = normal((M, C), 1.0)
+    W_fc = normal((C, F), w_std)
+    b_fc = normal((F,), b_std) if bias else None
+    W_proj = normal((F, C), proj_std)
+    b_proj = normal((C,), b_std) if bias else None
+    res = normal((M, C), 1.0) if with_residual else None
+    rd = lambda a: None if a is None else to_dtype(a, dtype)  # noqa: E731
+    return MlpInputs(rd(x), rd(W_fc), rd(b_fc), rd(W_proj), rd(b_proj), rd(res))
+
+
 def to_torch(a: np.ndarray | None, dtype: str, device="cpu"):
     """Host float32 array (already representable in ``dtype``) -> torch
     tensor of that dtype on ``device``; bf16 goes through its bit pattern so

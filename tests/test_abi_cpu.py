@@ -1,5 +1,5 @@
 """CPU checks of the C ABI: the library loads, exports every function that
-``include/gpt_attn.h`` declares, and its host-only paths (argument
+``include/gpt_attn.h`` and ``include/gpt_block.h`` declare, and its host-only paths (argument
 validation, workspace sizing, status strings) behave as documented.  No
 compute call is made here."""
 from __future__ import annotations
@@ -13,12 +13,15 @@ import pytest
 from gpt_causal_self_amd import gpt_attn as ga
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gpt_attn.h")
+HEADERS = [os.path.join(ROOT, "include", n) for n in ("gpt_attn.h", "gpt_block.h")]
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:const char \*|int )\s*(gpt_attn_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        names |= set(re.findall(r"^(?:const char \*|int )\s*(gpt_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -94,3 +97,24 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ga, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ga.lib()
+
+
+def test_block_entry_points_validate_on_the_host(lib):
+    """Argument errors of the Block entry points return before any device
+    call (no GPU here)."""
+    p = ctypes.c_void_p(4096)      # aligned, never dereferenced
+    odd = ctypes.c_void_p(4098)    # not 16-byte aligned
+    L = lib
+    assert L.gpt_layernorm(None, 4, 64, p, p, p, None) == ga.ERR_INVALID_ARG
+    assert L.gpt_layernorm(p, -1, 64, p, p, p, None) == ga.ERR_INVALID_ARG
+    assert L.gpt_layernorm(p, 4, 0, p, p, p, None) == ga.ERR_INVALID_ARG
+    assert L.gpt_layernorm(p, 4, 60, p, p, p, None) == ga.ERR_SHAPE
+    assert L.gpt_layernorm(p, 4, 8200, p, p, p, None) == ga.ERR_SHAPE
+    assert L.gpt_layernorm(odd, 4, 64, p, p, p, None) == ga.ERR_ALIGN
+    assert L.gpt_layernorm(p, 0, 64, p, None, p, None) == ga.OK       # empty: no-op
+    assert L.gpt_mlp_forward(p, 4, 64, 256, None, p, p, p, None, p, p, None) == ga.ERR_INVALID_ARG
+    assert L.gpt_mlp_forward(p, 4, 64, 250, p, p, p, p, None, p, p, None) == ga.ERR_SHAPE
+    assert L.gpt_mlp_forward(p, 4, 64, 256, p, p, p, p, odd, p, p, None) == ga.ERR_ALIGN
+    assert L.gpt_mlp_forward(p, 0, 64, 256, p, None, p, None, None, p, p, None) == ga.OK
+    assert L.gpt_attn_block_forward(None, p, 1, 1, p, p, p, p, p, p, 4, p, None) \
+        == ga.ERR_INVALID_ARG
