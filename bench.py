@@ -293,9 +293,10 @@ def time_calls(fn, n, warm=3):
 
 
 def next_rows(n=50):
-    """Timings of the Block pieces at the GPT-2 124M shape (B=12, T=1024,
-    C=768, 12 heads, MLP width 3072): LayerNorm, the Pre-LN attention
-    half-block and the MLP sublayer with its residual add."""
+    """Timings of the pieces around the layer at the GPT-2 124M shape (B=12,
+    T=1024, C=768, 12 heads, MLP width 3072): LayerNorm, the Pre-LN attention
+    half-block, one-token decode against a full KV cache, and the MLP
+    sublayer with its residual add."""
     import torch
     from gpt_causal_self_amd import gpt_attn as ga
     from gpt_causal_self_amd.inputs import (WORKLOADS, make_inputs, make_ln_params,
@@ -328,6 +329,23 @@ def next_rows(n=50):
                               "ms": round(ms, 5),
                               "tflops": round(F_blk / (ms * 1e-3) / 1e12, 2),
                               "tokens_per_s": round(M / (ms * 1e-3), 1)}
+    # one-token decode at the last position of a full 1024-token cache
+    hs = C // H
+    kc = torch.randn((B, H, T, hs), device=dev).to(torch.bfloat16)
+    vc = torch.randn((B, H, T, hs), device=dev).to(torch.bfloat16)
+    xt = t["x"][:, T - 1].contiguous()
+    yt = torch.empty_like(xt)
+    ms = time_calls(lambda: ga.gpt_attn_decode(layer.h, xt, t["W_attn"], t["b_attn"],
+                                               t["W_proj"], t["b_proj"], H, kc, vc, yt, T - 1), n)
+    dec_bytes = 2 * B * H * T * hs * 2 + (4 * C * C + 4 * C) * 2 + 4 * B * C * 2
+    res["decode"] = {"workload": f"one token per sequence at pos={T - 1}, B={B} C={C} H={H}, "
+                                 f"bf16 KV cache of {T} positions",
+                     "ms": round(ms, 5), "tokens_per_s": round(B / (ms * 1e-3), 1),
+                     "roofline": {"bound": "hbm",
+                                  "achieved": round(dec_bytes / (ms * 1e-3) / 1e9, 1),
+                                  "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                  "frac": round(dec_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                                  "algorithmic_bytes": dec_bytes}}
     layer.close()
     m = make_mlp_inputs(M, C, F, seed=127, with_residual=True)
     d = {k: to_torch(getattr(m, k), "bf16", dev)

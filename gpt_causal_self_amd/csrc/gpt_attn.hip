@@ -74,6 +74,7 @@ int gpt_attn_create(gpt_attn_t* out, int C, int n_head, int max_B, int max_T, in
   h->part = (float*)(h->ws + L.part);
   h->part_elems = L.part_elems;
   h->ln = h->ws + L.ln;
+
   *out = h;
   return GPT_ATTN_OK;
 }
@@ -130,6 +131,7 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
       (b_attn && !aligned16(b_attn)) || (b_proj && !aligned16(b_proj)))
     return GPT_ATTN_ERR_ALIGN;
   h->saved = 0;
+  h->last_B = h->last_T = 0;
   if (B == 0 || T == 0) {  // nothing to compute; an empty backward may follow
     if (save_for_backward) {
       h->saved = 1;
@@ -172,6 +174,8 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
     mark(h, 3, st);
   }
   const int rc = launch_status();
+  h->last_B = rc == GPT_ATTN_OK ? B : 0;
+  h->last_T = rc == GPT_ATTN_OK ? T : 0;
   if (rc == GPT_ATTN_OK && save_for_backward) {
     h->saved = 1;
     h->saved_B = B;

@@ -49,6 +49,7 @@ int gpt_attn_block_forward(gpt_attn_t h, const void* x, int B, int T, const void
       (b_proj && !aligned16(b_proj)))
     return GPT_ATTN_ERR_ALIGN;
   h->saved = 0;  // the workspace no longer holds a plain forward's state
+  h->last_B = h->last_T = 0;
   if (B == 0 || T == 0) return GPT_ATTN_OK;
   const hipStream_t st = as_stream(stream);
   const int M = B * T;
@@ -57,7 +58,12 @@ int gpt_attn_block_forward(gpt_attn_t h, const void* x, int B, int T, const void
   layer_forward_bf16(h, ln, B, T, (const bf16_t*)W_attn, (const bf16_t*)b_attn,
                      (const bf16_t*)W_proj, (const bf16_t*)b_proj, (bf16_t*)out,
                      (const bf16_t*)x, nullptr, st);
-  return launch_status();
+  const int rc = launch_status();
+  if (rc == GPT_ATTN_OK) {
+    h->last_B = B;
+    h->last_T = T;
+  }
+  return rc;
 }
 
 int gpt_mlp_forward(const void* x, int M, int C, int F, const void* W_fc, const void* b_fc,

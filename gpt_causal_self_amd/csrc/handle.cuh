@@ -54,6 +54,8 @@ struct gpt_attn_handle {
   size_t part_elems;
   // state of the last forward
   int saved, saved_B, saved_T;
+  // q/k/v of the last forward (any kind) still in the workspace: B, T
+  int last_B, last_T;
   // optional stage events (measurement hook)
   hipEvent_t ev[8];
   int n_ev;

@@ -1,5 +1,5 @@
-"""Thin ctypes binding of ``libgpt_attn.so`` (C ABI in ``include/gpt_attn.h``
-and ``include/gpt_block.h``).
+"""Thin ctypes binding of ``libgpt_attn.so`` (C ABI in ``include/gpt_attn.h``,
+``include/gpt_block.h`` and ``include/gpt_decode.h``).
 
 Argument marshalling only: torch tensors supply device memory and
 ``torch.cuda.current_stream()`` supplies the stream; every step of the layer
@@ -22,7 +22,7 @@ EXPORTED = ("gpt_attn_workspace_bytes", "gpt_attn_create", "gpt_attn_forward",
             "gpt_attn_backward", "gpt_attn_destroy", "gpt_attn_strerror",
             "gpt_attn_debug_workspace", "gpt_attn_set_stage_events",
             "gpt_attn_debug_backward", "gpt_layernorm", "gpt_attn_block_forward",
-            "gpt_mlp_forward")
+            "gpt_mlp_forward", "gpt_attn_decode", "gpt_attn_export_kv")
 
 _lib = None
 
@@ -58,6 +58,8 @@ def lib():
         L.gpt_layernorm.argtypes = [vp, i, i, vp, vp, vp, vp]
         L.gpt_attn_block_forward.argtypes = [vp, vp, i, i, vp, vp, vp, vp, vp, vp, i, vp, vp]
         L.gpt_mlp_forward.argtypes = [vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.gpt_attn_decode.argtypes = [vp, vp, i, i, vp, vp, vp, vp, i, vp, vp, i, vp, vp]
+        L.gpt_attn_export_kv.argtypes = [vp, vp, vp, i, vp]
         for name in EXPORTED:
             if name != "gpt_attn_strerror":
                 getattr(L, name).restype = i
@@ -188,6 +190,28 @@ def gpt_mlp_forward(x, W_fc, b_fc, W_proj, b_proj, hbuf, y, residual=None, strea
                                _ptr(b_proj), _ptr(residual), _ptr(hbuf), _ptr(y),
                                _stream(stream))
     _check(rc, "gpt_mlp_forward")
+
+
+def gpt_attn_decode(h, x_new, W_attn, b_attn, W_proj, b_proj, n_head, k_cache, v_cache, y,
+                    pos, stream=None, B=None, cache_T=None):
+    """One decode step at position pos: x_new [B, C] -> y [B, C]; k_cache and
+    v_cache [B, H, cache_T, hs] receive this position's key and value."""
+    if B is None:
+        B = int(x_new.shape[0])
+    if cache_T is None:
+        cache_T = int(k_cache.shape[2])
+    rc = lib().gpt_attn_decode(h, _ptr(x_new), B, pos, _ptr(W_attn), _ptr(b_attn), _ptr(W_proj),
+                               _ptr(b_proj), n_head, _ptr(k_cache), _ptr(v_cache), cache_T,
+                               _ptr(y), _stream(stream))
+    _check(rc, "gpt_attn_decode")
+
+
+def gpt_attn_export_kv(h, k_cache, v_cache, stream=None, cache_T=None):
+    """Copy the keys and values of the last forward into the caches."""
+    if cache_T is None:
+        cache_T = int(k_cache.shape[2])
+    _check(lib().gpt_attn_export_kv(h, _ptr(k_cache), _ptr(v_cache), cache_T, _stream(stream)),
+           "gpt_attn_export_kv")
 
 
 class Layer:

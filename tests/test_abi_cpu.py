@@ -1,5 +1,6 @@
 """CPU checks of the C ABI: the library loads, exports every function that
-``include/gpt_attn.h`` and ``include/gpt_block.h`` declare, and its host-only paths (argument
+``include/gpt_attn.h``, ``include/gpt_block.h`` and ``include/gpt_decode.h``
+declare, and its host-only paths (argument
 validation, workspace sizing, status strings) behave as documented.  No
 compute call is made here."""
 from __future__ import annotations
@@ -13,7 +14,7 @@ import pytest
 from gpt_causal_self_amd import gpt_attn as ga
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", n) for n in ("gpt_attn.h", "gpt_block.h")]
+HEADERS = [os.path.join(ROOT, "include", n) for n in ("gpt_attn.h", "gpt_block.h", "gpt_decode.h")]
 
 
 def declared_functions():
@@ -118,3 +119,10 @@ def test_block_entry_points_validate_on_the_host(lib):
     assert L.gpt_mlp_forward(p, 0, 64, 256, p, None, p, None, None, p, p, None) == ga.OK
     assert L.gpt_attn_block_forward(None, p, 1, 1, p, p, p, p, p, p, 4, p, None) \
         == ga.ERR_INVALID_ARG
+
+
+def test_decode_entry_points_validate_on_the_host(lib):
+    p = ctypes.c_void_p(4096)
+    L = lib
+    assert L.gpt_attn_decode(None, p, 1, 0, p, p, p, p, 4, p, p, 8, p, None) == ga.ERR_INVALID_ARG
+    assert L.gpt_attn_export_kv(None, p, p, 8, None) == ga.ERR_INVALID_ARG
