@@ -60,6 +60,18 @@ def _declare(lib):
     lib.oracle_backward.restype = i
     lib.oracle_backward.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
                                     dp, dp, dp, dp, dp, dp, dp, i, i]
+    u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.oracle_philox4x32_10.restype = None
+    lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
+    lib.oracle_dropout_threshold.restype = ctypes.c_uint32
+    lib.oracle_dropout_threshold.argtypes = [ctypes.c_double]
+    lib.oracle_dropout_keep_attn.restype = i
+    lib.oracle_dropout_keep_attn.argtypes = [i, i, i, i, i, ctypes.c_uint64, ctypes.c_uint32]
+    lib.oracle_dropout_keep_resid.restype = i
+    lib.oracle_dropout_keep_resid.argtypes = [ctypes.c_long, i, ctypes.c_uint64, ctypes.c_uint32]
+    lib.oracle_forward_dropout.restype = i
+    lib.oracle_forward_dropout.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, ctypes.c_double,
+                                           ctypes.c_uint64, dp, dp, i, i]
     return lib
 
 
@@ -227,3 +239,53 @@ def mlp_forward(x, W_fc, b_fc, W_proj, b_proj, *, want_h=False, store_bf16=(),
     if rc != 0:
         raise ValueError("oracle_mlp_forward failed")
     return {"y": y, "h": h} if want_h else {"y": y}
+
+
+def philox4x32_10(ctr, key, *, lib=None):
+    """Philox4x32-10 of a 4-word counter and a 2-word key -> 4 words."""
+    lib = lib or load()
+    c = (ctypes.c_uint32 * 4)(*[int(v) & 0xFFFFFFFF for v in ctr])
+    k = (ctypes.c_uint32 * 2)(*[int(v) & 0xFFFFFFFF for v in key])
+    o = (ctypes.c_uint32 * 4)()
+    lib.oracle_philox4x32_10(c, k, o)
+    return [int(v) for v in o]
+
+
+def dropout_threshold(p, *, lib=None):
+    return int((lib or load()).oracle_dropout_threshold(float(p)))
+
+
+def dropout_keep_attn(b, h, H, i, j, p, seed, *, lib=None):
+    lib = lib or load()
+    return bool(lib.oracle_dropout_keep_attn(b, h, H, i, j, int(seed),
+                                             lib.oracle_dropout_threshold(float(p))))
+
+
+def dropout_keep_resid(m, n, p, seed, *, lib=None):
+    lib = lib or load()
+    return bool(lib.oracle_dropout_keep_resid(m, n, int(seed),
+                                              lib.oracle_dropout_threshold(float(p))))
+
+
+def forward_dropout(x, W_attn, b_attn, W_proj, b_proj, n_head, p, seed, *, want_ym=False,
+                    store_bf16=(), nthreads=None, lib=None):
+    """Forward with dropout rate p on the attention weights and on the c_proj
+    output (Philox masks keyed by ``seed``); fp64.  ``store_bf16`` may name
+    "qkv" and "ym"."""
+    lib = lib or load()
+    x = _f64(x)
+    B, T, C = x.shape
+    W_attn, b_attn, W_proj, b_proj = map(_f64, (W_attn, b_attn, W_proj, b_proj))
+    y = np.empty((B, T, C))
+    ym = np.empty((B, T, C)) if want_ym else None
+    rc = lib.oracle_forward_dropout(
+        B, T, C, int(n_head), _ptr(x), _ptr(W_attn), _ptr(b_attn), _ptr(W_proj), _ptr(b_proj),
+        float(p), int(seed), _ptr(y), _ptr(ym),
+        (1 if "qkv" in store_bf16 else 0) | (2 if "ym" in store_bf16 else 0),
+        int(nthreads or default_threads()))
+    if rc != 0:
+        raise ValueError("oracle_forward_dropout failed (bad arguments or out of memory)")
+    out = {"y": y}
+    if want_ym:
+        out["ym"] = ym
+    return out

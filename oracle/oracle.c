@@ -49,12 +49,21 @@
  * flow", section 3 training loop).  The softmax gradient uses the Jacobian
  * form dS_ij = p_ij (dP_ij - sum_j' p_ij' dP_ij').
  *
+ * Dropout (training; nn.Dropout on the attention weights after the softmax
+ * and on the c_proj output, page "nanoGPT architecture explained step by
+ * step", section 3, attn_dropout / resid_dropout; rate config.dropout) is
+ * available as a separate entry point.  Each element keeps or drops on a
+ * 32-bit word of the Philox4x32-10 counter-based generator (Salmon, Moraes,
+ * Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011):
+ * dropped iff word < floor(p * 2^32); kept values are scaled by 1/(1-p).
+ *
  * Everything is double precision; callers pass the exact values the GPU
  * receives (bf16 and fp32 upcast exactly).  Work is split over threads by
  * output rows or by (batch, head) pairs only; no sum is reordered.
  */
 #include <math.h>
 #include <pthread.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -497,5 +506,137 @@ int oracle_mlp_forward(int M, int C, int F, const double *x, const double *W_fc,
   rc = 0;
 done:
   if (!h_out) free(h);
+  return rc;
+}
+
+
+/* ------------------------------------------------------------------ */
+/* Philox4x32-10 and dropout.                                          */
+/* ------------------------------------------------------------------ */
+/* One Philox4x32 round: two 32x32->64 products of counter words 0 and 2 by
+ * the round multipliers; the high halves are mixed with words 1 and 3 and
+ * the round key, the low halves move to words 1 and 3.  Between rounds the
+ * key advances by the Weyl constants.  Ten rounds (Salmon et al., SC 2011,
+ * section 4, Philox-4x32 with R = 10). */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+  uint32_t k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * x0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * x2;
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    x0 = hi1 ^ x1 ^ k0;
+    x1 = lo1;
+    x2 = hi0 ^ x3 ^ k1;
+    x3 = lo0;
+  }
+  out[0] = x0;
+  out[1] = x1;
+  out[2] = x2;
+  out[3] = x3;
+}
+
+/* Drop threshold of rate p: a 32-bit word w drops its element iff w < t,
+ * t = floor(p * 2^32) (capped at 2^32 - 1), so P(drop) = t / 2^32. */
+uint32_t oracle_dropout_threshold(double p) {
+  const double t = floor(p * 4294967296.0);
+  return t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+}
+
+/* Keep decision of one element: the word (c0 & 3) of Philox(ctr = {c0 >> 2,
+ * c1, c2, stream}, key = seed split into low / high 32 bits). */
+static int keep_elem(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t stream, uint64_t seed,
+                     uint32_t thresh) {
+  const uint32_t ctr[4] = {c0 >> 2, c1, c2, stream};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t w[4];
+  oracle_philox4x32_10(ctr, key, w);
+  return w[c0 & 3] >= thresh;
+}
+
+/* Keep mask of the attention weights of head (b, h), query i, key j:
+ * stream 1, counter words (j, i, b*H + h); of the c_proj output element
+ * (row m = b*T + t, column n): stream 2, counter words (n, m, 0). */
+int oracle_dropout_keep_attn(int b, int h, int H, int i, int j, uint64_t seed, uint32_t thresh) {
+  return keep_elem((uint32_t)j, (uint32_t)i, (uint32_t)(b * H + h), 1u, seed, thresh);
+}
+int oracle_dropout_keep_resid(long m, int n, uint64_t seed, uint32_t thresh) {
+  return keep_elem((uint32_t)n, (uint32_t)m, 0u, 2u, seed, thresh);
+}
+
+typedef struct {
+  int B, T, C, H;
+  const double *qkv;
+  double *ym;
+  double p;
+  uint64_t seed;
+  uint32_t thresh;
+} drop_attn_ctx;
+
+/* Head (b, h) with dropout on the softmax weights: the row is normalised
+ * over all visible keys first, then each weight is dropped or scaled by
+ * 1/(1-p) before it weights its value row. */
+static void drop_attn_head(void *vctx, long item, double *p) {
+  const drop_attn_ctx *c = (const drop_attn_ctx *)vctx;
+  const int b = (int)(item / c->H), h = (int)(item % c->H);
+  const int T = c->T, C = c->C, H = c->H, hs = C / H;
+  const size_t ld = (size_t)3 * C;
+  const double keep_scale = 1.0 / (1.0 - c->p);
+  for (int i = 0; i < T; ++i) {
+    prob_row(c->qkv, T, C, H, b, h, i, p);
+    double *o = c->ym + ((size_t)b * T + i) * C + (size_t)h * hs;
+    for (int d = 0; d < hs; ++d) o[d] = 0.0;
+    for (int j = 0; j <= i; ++j) {
+      if (!oracle_dropout_keep_attn(b, h, H, i, j, c->seed, c->thresh)) continue;
+      const double w = p[j] * keep_scale;
+      const double *v = c->qkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;
+      for (int d = 0; d < hs; ++d) o[d] += w * v[d];
+    }
+  }
+}
+
+/* Forward with dropout rate p (0 <= p < 1) on the attention weights and on
+ * the c_proj output, masks from Philox keyed by `seed` as above.  Arguments
+ * otherwise as oracle_forward (ym_out optional; store_bf16 bits 0 / 1 round
+ * qkv / merged heads).  p = 0 keeps everything (same result as
+ * oracle_forward). */
+int oracle_forward_dropout(int B, int T, int C, int H, const double *x, const double *W_attn,
+                           const double *b_attn, const double *W_proj, const double *b_proj,
+                           double p, uint64_t seed, double *y, double *ym_out, int store_bf16,
+                           int nthreads) {
+  if (B < 0 || T < 0 || C <= 0 || H <= 0 || C % H != 0) return -1;
+  if (!x || !W_attn || !W_proj || !y || !(p >= 0.0 && p < 1.0)) return -1;
+  const long M = (long)B * T;
+  if (M == 0) return 0;
+  const uint32_t thresh = oracle_dropout_threshold(p);
+  double *qkv = (double *)malloc((size_t)M * 3 * C * sizeof(double));
+  double *ym = ym_out ? ym_out : (double *)malloc((size_t)M * C * sizeof(double));
+  int rc = -1;
+  if (!qkv || !ym) goto done;
+  if (linear((int)M, C, 3 * C, x, W_attn, b_attn, qkv, nthreads)) goto done;
+  if (store_bf16 & 1) round_all(qkv, (size_t)M * 3 * C);
+  {
+    drop_attn_ctx a = {B, T, C, H, qkv, ym, p, seed, thresh};
+    if (parallel_for((long)B * H, nthreads, drop_attn_head, &a, (size_t)T)) goto done;
+  }
+  if (store_bf16 & 2) round_all(ym, (size_t)M * C);
+  if (linear((int)M, C, C, ym, W_proj, b_proj, y, nthreads)) goto done;
+  {
+    const double keep_scale = 1.0 / (1.0 - p);
+    for (long m = 0; m < M; ++m)
+      for (int n = 0; n < C; ++n)
+        y[(size_t)m * C + n] = oracle_dropout_keep_resid(m, n, seed, thresh)
+                                   ? y[(size_t)m * C + n] * keep_scale
+                                   : 0.0;
+  }
+  rc = 0;
+done:
+  free(qkv);
+  if (!ym_out) free(ym);
   return rc;
 }

@@ -1,0 +1,89 @@
+"""Pins of the oracle's dropout: the Philox4x32-10 generator against its
+published known-answer vectors, the drop threshold, the keep rate, p = 0 as
+the identity, and the composition (weights dropped after the softmax and
+rescaled by 1/(1-p), c_proj output dropped after its bias) against a numpy
+assembly of the separately pinned pieces on a tiny case."""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpt_causal_self_amd.inputs import make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
+
+
+def _kat():
+    rows = []
+    for line in open(GOLDEN):
+        if line.startswith("#") or not line.strip():
+            continue
+        w = [int(t, 16) for t in line.split()]
+        rows.append((w[:4], w[4:6], w[6:10]))
+    return rows
+
+
+@pytest.mark.parametrize("ctr,key,want", _kat())
+def test_philox_known_answers(ctr, key, want):
+    assert oracle.philox4x32_10(ctr, key) == want
+
+
+def test_threshold():
+    assert oracle.dropout_threshold(0.0) == 0
+    assert oracle.dropout_threshold(0.5) == 1 << 31
+    assert oracle.dropout_threshold(0.1) == 429496729          # floor(0.1 * 2^32)
+    assert oracle.dropout_threshold(0.9999999999999999) == 0xFFFFFFFF
+
+
+def test_keep_rate_and_independence():
+    p, seed = 0.3, 1234
+    keep = np.array([oracle.dropout_keep_attn(0, 1, 4, i, j, p, seed)
+                     for i in range(64) for j in range(64)], dtype=float)
+    n = keep.size
+    assert abs(keep.mean() - (1 - p)) < 5 * np.sqrt(p * (1 - p) / n)
+    res = np.array([oracle.dropout_keep_resid(m, n_, p, seed)
+                    for m in range(64) for n_ in range(64)], dtype=float)
+    assert abs(res.mean() - (1 - p)) < 5 * np.sqrt(p * (1 - p) / n)
+    # the two streams and different seeds give different masks
+    assert np.mean(keep != res) > 0.2
+    other = np.array([oracle.dropout_keep_attn(0, 1, 4, i, j, p, seed + 1)
+                      for i in range(64) for j in range(64)], dtype=float)
+    assert np.mean(keep != other) > 0.2
+
+
+def test_p_zero_is_the_plain_forward():
+    inp = make_inputs(2, 19, 32, 4, dtype="f32", seed=3, w_std=0.3, proj_std=0.3)
+    a = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, 4)["y"]
+    b = oracle.forward_dropout(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, 4,
+                               0.0, 99)["y"]
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("p", [0.5, 0.1])
+def test_composition_on_a_tiny_case(p):
+    B, T, C, H = 2, 6, 8, 2
+    hs = C // H
+    seed = 77
+    inp = make_inputs(B, T, C, H, dtype="f32", seed=11, w_std=0.4, proj_std=0.4,
+                      b_attn_std=0.2, b_proj_std=0.2)
+    r = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, H,
+                       want=("P", "qkv"))
+    P, qkv = r["P"], r["qkv"]
+    ym = np.zeros((B, T, C))
+    for b in range(B):
+        for h in range(H):
+            v = qkv[b, :, 2 * C + h * hs:2 * C + (h + 1) * hs]
+            Z = np.array([[oracle.dropout_keep_attn(b, h, H, i, j, p, seed) for j in range(T)]
+                          for i in range(T)], dtype=float)
+            ym[b, :, h * hs:(h + 1) * hs] = (P[b, h] * Z / (1 - p)) @ v
+    y = ym @ inp.W_proj + inp.b_proj
+    Z2 = np.array([[oracle.dropout_keep_resid(b * T + t, n, p, seed) for n in range(C)]
+                   for b in range(B) for t in range(T)], dtype=float).reshape(B, T, C)
+    y = y * Z2 / (1 - p)
+    got = oracle.forward_dropout(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, H,
+                                 p, seed, want_ym=True)
+    np.testing.assert_allclose(got["ym"], ym, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(got["y"], y, rtol=1e-12, atol=1e-14)

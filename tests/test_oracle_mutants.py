@@ -68,6 +68,13 @@ MUTANTS = [
        "return u * 0.5 * (1.0 + tanh(0.7978845608028654 * (u + 0.044715 * u * u * u)));", 0)]),
     ("block drops the residual", [("out[i] = x[i] + y[i];", "out[i] = y[i];", 0)]),
     ("mlp skips gelu", [("h[i] = gelu(h[i]);", "h[i] = h[i];", 0)]),
+    ("philox multiplier", [("(uint64_t)0xD2511F53u * x0", "(uint64_t)0xD2511F57u * x0", 0)]),
+    ("philox key schedule", [("k0 += 0x9E3779B9u;", "k0 += 0x9E3779B1u;", 0)]),
+    ("dropout weights not rescaled", [("const double w = p[j] * keep_scale;",
+                                       "const double w = p[j];", 0)]),
+    ("residual dropout not rescaled", [("? y[(size_t)m * C + n] * keep_scale",
+                                        "? y[(size_t)m * C + n]", 0)]),
+    ("dropout word index", [("return w[c0 & 3] >= thresh;", "return w[0] >= thresh;", 0)]),
     ("input grad with untransposed square weight",
      [("s += g[n] * w[n];",
        "s += g[n] * (c->K == c->N ? c->W[(size_t)n * c->N + k] : w[n]);", 0)]),
@@ -116,6 +123,37 @@ def _pins(lib):
     yb = oracle.forward(lnb, inb.W_attn, inb.b_attn, inb.W_proj, inb.b_proj, 2, lib=lib)["y"]
     if not np.allclose(ob, inb.x + yb, rtol=1e-12, atol=1e-13):
         failed.append("block")
+    # dropout: Philox known answers, the element -> counter mapping, and the
+    # composition against a numpy assembly of the pinned pieces
+    import test_oracle_dropout_pins as dpin
+    for ctr, key, want in dpin._kat():
+        if oracle.philox4x32_10(ctr, key, lib=lib) != want:
+            failed.append("philox kat")
+            break
+    thr = oracle.dropout_threshold(0.5, lib=lib)
+    for (i, j) in ((3, 5), (7, 0), (9, 14)):
+        w = oracle.philox4x32_10([j >> 2, i, 1 * 4 + 2, 1], [77, 0], lib=lib)[j & 3]
+        if oracle.dropout_keep_attn(1, 2, 4, i, j, 0.5, 77, lib=lib) != (w >= thr):
+            failed.append("dropout mapping")
+            break
+    pd, sd = 0.5, 77
+    di = make_inputs(1, 5, 8, 2, dtype="f32", seed=11, w_std=0.4, proj_std=0.4,
+                     b_attn_std=0.2, b_proj_std=0.2)
+    r = oracle.forward(di.x, di.W_attn, di.b_attn, di.W_proj, di.b_proj, 2,
+                       want=("P", "qkv"), lib=lib)
+    ymd = np.zeros((1, 5, 8))
+    for h in range(2):
+        Z = np.array([[oracle.dropout_keep_attn(0, h, 2, i, j, pd, sd, lib=lib)
+                       for j in range(5)] for i in range(5)], dtype=float)
+        ymd[0, :, 4 * h:4 * h + 4] = (r["P"][0, h] * Z / (1 - pd)) @ r["qkv"][0, :, 16 + 4 * h:20 + 4 * h]
+    yd = ymd @ di.W_proj + di.b_proj
+    Z2 = np.array([[oracle.dropout_keep_resid(t, n, pd, sd, lib=lib) for n in range(8)]
+                   for t in range(5)], dtype=float)[None]
+    yd = yd * Z2 / (1 - pd)
+    got = oracle.forward_dropout(di.x, di.W_attn, di.b_attn, di.W_proj, di.b_proj, 2, pd, sd,
+                                 lib=lib)["y"]
+    if not np.allclose(got, yd, rtol=1e-12, atol=1e-14):
+        failed.append("dropout composition")
     # brute force forward, incl. P and the log-sum-exp
     for (B, T, C, H, bias) in ((2, 5, 8, 2, True), (2, 6, 16, 4, False)):
         inp = make_inputs(B, T, C, H, bias=bias, dtype="f32", seed=T, w_std=0.5,
