@@ -30,6 +30,7 @@
 
 #include "common.cuh"
 #include "gemm2.cuh"
+#include "philox.cuh"
 
 namespace gpt_attn {
 
@@ -54,11 +55,14 @@ __device__ __forceinline__ int kv_swz(int row) {
   return HS == 64 ? (row & 7) : ((row >> 1) & 3);
 }
 
-template <int HS, int NS>
+// DROP: dropout on the attention weights (philox.cuh): the row sum uses
+// every weight, the P.V product only the kept ones, and the output is scaled
+// by 1 / (1 - p).
+template <int HS, int NS, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kg,
     const bf16_t* __restrict__ Vg, bf16_t* __restrict__ O, float* __restrict__ lse,
-    int H, int T, float scale_log2) {
+    int H, int T, float scale_log2, DropParams drop = {}) {
   static_assert(HS == 32 || HS == 64, "head size");
   constexpr int BKV = kAttnBK;
   constexpr int TILE = BKV * HS * 2;   // bytes of one K or V tile
@@ -216,6 +220,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
       }
     rs += __shfl_xor(rs, 32);
     l += rs;
+    if constexpr (DROP) {
+      // keys j0 + kt*32 + 8g + 4hi + e (e = 0..3) of query myq: one Philox
+      // call covers the 4 consecutive keys of register group g
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t jb = (uint32_t)(j0 + kt * 32 + 8 * g + 4 * hi);
+          const uint4 w = philox4x32_10(make_uint4(jb >> 2, (uint32_t)myq, (uint32_t)bh, 1u),
+                                        drop.k0, drop.k1);
+          if (w.x < drop.thresh) sc[kt][4 * g + 0] = 0.f;
+          if (w.y < drop.thresh) sc[kt][4 * g + 1] = 0.f;
+          if (w.z < drop.thresh) sc[kt][4 * g + 2] = 0.f;
+          if (w.w < drop.thresh) sc[kt][4 * g + 3] = 0.f;
+        }
+    }
     // ---- O^T += V^T P^T; V^T operand by transposing reads in the key order
     // of the P registers: element e <-> key kb + 8(e/4) + 4*hi + e%4.
     int va[HS / 32];
@@ -275,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
   }
 
   if (myq < T) {
-    const float inv = 1.f / l;
+    const float inv = (DROP ? drop.scale : 1.f) / l;
     const int C = HS * H;
     bf16_t* orow = O + ((size_t)b * T + myq) * C + h * HS;
 #pragma unroll

@@ -150,9 +150,10 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
   (void)M;
 
   if (h->dtype == GPT_ATTN_BF16) {
+    const DropParams drop = make_drop(h->drop_p, h->drop_seed);
     layer_forward_bf16(h, (const bf16_t*)x, B, T, (const bf16_t*)W_attn, (const bf16_t*)b_attn,
                        (const bf16_t*)W_proj, (const bf16_t*)b_proj, (bf16_t*)y, nullptr, lse,
-                       st);
+                       st, h->drop_p > 0.f ? &drop : nullptr);
   } else {
     const float* xf = (const float*)x;
     float* qkv = (float*)h->qkv;
@@ -180,8 +181,18 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
     h->saved = 1;
     h->saved_B = B;
     h->saved_T = T;
+    h->saved_drop_p = h->drop_p;
+    h->saved_drop_seed = h->drop_seed;
   }
   return rc;
+}
+
+int gpt_attn_set_dropout(gpt_attn_t h, float p, unsigned long long seed) {
+  if (!h || !(p >= 0.f && p < 1.f)) return GPT_ATTN_ERR_INVALID_ARG;
+  if (p > 0.f && h->dtype != GPT_ATTN_BF16) return GPT_ATTN_ERR_UNSUPPORTED;
+  h->drop_p = p;
+  h->drop_seed = seed;
+  return GPT_ATTN_OK;
 }
 
 int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const void* W_proj,
@@ -197,6 +208,7 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
       (db_attn && !aligned16(db_attn)) || (db_proj && !aligned16(db_proj)))
     return GPT_ATTN_ERR_ALIGN;
   if (!h->saved || h->saved_B != B || h->saved_T != T) return GPT_ATTN_ERR_STATE;
+  if (h->saved_drop_p > 0.f) return GPT_ATTN_ERR_UNSUPPORTED;
 
   const int C = h->C, H = h->H, hs = h->hs;
   const int M = B * T, N3 = 3 * C;

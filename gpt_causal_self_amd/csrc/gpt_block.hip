@@ -55,9 +55,10 @@ int gpt_attn_block_forward(gpt_attn_t h, const void* x, int B, int T, const void
   const int M = B * T;
   bf16_t* ln = (bf16_t*)h->ln;
   launch_layernorm((const bf16_t*)x, (const bf16_t*)ln_w, (const bf16_t*)ln_b, ln, M, h->C, st);
+  const DropParams drop = make_drop(h->drop_p, h->drop_seed);
   layer_forward_bf16(h, ln, B, T, (const bf16_t*)W_attn, (const bf16_t*)b_attn,
                      (const bf16_t*)W_proj, (const bf16_t*)b_proj, (bf16_t*)out,
-                     (const bf16_t*)x, nullptr, st);
+                     (const bf16_t*)x, nullptr, st, h->drop_p > 0.f ? &drop : nullptr);
   const int rc = launch_status();
   if (rc == GPT_ATTN_OK) {
     h->last_B = B;

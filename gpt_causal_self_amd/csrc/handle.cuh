@@ -8,6 +8,7 @@
 #include <math.h>
 
 #include "../../include/gpt_attn.h"
+#include "philox.cuh"
 
 // Tile shapes (BM, BN, pipeline stages, BK, wave grid rows, wave grid columns)
 // of the bf16 GEMMs.
@@ -56,6 +57,12 @@ struct gpt_attn_handle {
   int saved, saved_B, saved_T;
   // q/k/v of the last forward (any kind) still in the workspace: B, T
   int last_B, last_T;
+  // dropout rate and generator seed of later forwards (0: none); the rate
+  // and seed of the saved forward
+  float drop_p;
+  unsigned long long drop_seed;
+  float saved_drop_p;
+  unsigned long long saved_drop_seed;
   // optional stage events (measurement hook)
   hipEvent_t ev[8];
   int n_ev;
@@ -109,6 +116,17 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 inline void mark(const gpt_attn_handle* h, int i, hipStream_t st) {
   if (i < h->n_ev) (void)hipEventRecord(h->ev[i], st);
+}
+
+// Dropout parameters of rate p and seed (philox.cuh).
+inline gpt_attn::DropParams make_drop(float p, unsigned long long seed) {
+  const double t = floor((double)p * 4294967296.0);
+  gpt_attn::DropParams d;
+  d.k0 = (uint32_t)seed;
+  d.k1 = (uint32_t)(seed >> 32);
+  d.thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  d.scale = (float)(1.0 / (1.0 - (double)p));
+  return d;
 }
 
 inline int launch_status() {

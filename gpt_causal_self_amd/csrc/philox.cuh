@@ -1,0 +1,43 @@
+// philox.cuh -- Philox4x32-10 counter-based generator and the dropout keep
+// rule of the layer.
+//
+// Philox4x32 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy
+// as 1, 2, 3", SC 2011): a 4-word counter is mixed with a 2-word key by ten
+// rounds; each round multiplies counter words 0 and 2 by two fixed odd
+// constants (32 x 32 -> 64 bits), xors the high halves with words 1 and 3
+// and the round key, and moves the low halves into words 1 and 3; the key
+// advances by two Weyl constants between rounds.
+//
+// Dropout (nn.Dropout after the softmax and after c_proj; page "nanoGPT
+// architecture explained step by step", section 3): an element is dropped
+// iff its word of Philox(counter, key = seed) is below t = floor(p * 2^32);
+// kept elements are scaled by 1 / (1 - p).  Attention weight (b, h, i, j):
+// counter (j / 4, i, b * H + h, 1), word j % 4.  c_proj output (m, n):
+// counter (n / 4, m, 0, 2), word n % 4.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace gpt_attn {
+
+struct DropParams {
+  uint32_t k0, k1;   // key: seed low / high word
+  uint32_t thresh;   // drop iff word < thresh
+  float scale;       // 1 / (1 - p)
+};
+
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, c.z), lo1 = 0xCD9E8D57u * c.z;
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+}  // namespace gpt_attn

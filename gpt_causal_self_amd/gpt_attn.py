@@ -22,7 +22,8 @@ EXPORTED = ("gpt_attn_workspace_bytes", "gpt_attn_create", "gpt_attn_forward",
             "gpt_attn_backward", "gpt_attn_destroy", "gpt_attn_strerror",
             "gpt_attn_debug_workspace", "gpt_attn_set_stage_events",
             "gpt_attn_debug_backward", "gpt_layernorm", "gpt_attn_block_forward",
-            "gpt_mlp_forward", "gpt_attn_decode", "gpt_attn_export_kv")
+            "gpt_mlp_forward", "gpt_attn_decode", "gpt_attn_export_kv",
+            "gpt_attn_set_dropout")
 
 _lib = None
 
@@ -60,6 +61,7 @@ def lib():
         L.gpt_mlp_forward.argtypes = [vp, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
         L.gpt_attn_decode.argtypes = [vp, vp, i, i, vp, vp, vp, vp, i, vp, vp, i, vp, vp]
         L.gpt_attn_export_kv.argtypes = [vp, vp, vp, i, vp]
+        L.gpt_attn_set_dropout.argtypes = [vp, ctypes.c_float, ctypes.c_ulonglong]
         for name in EXPORTED:
             if name != "gpt_attn_strerror":
                 getattr(L, name).restype = i
@@ -127,6 +129,12 @@ def gpt_attn_backward(h, x, W_attn, W_proj, dY, dx, dW_attn, db_attn, dW_proj, d
                                  _ptr(dW_attn), _ptr(db_attn), _ptr(dW_proj), _ptr(db_proj),
                                  B, T, _stream(stream))
     _check(rc, "gpt_attn_backward")
+
+
+def gpt_attn_set_dropout(h, p, seed):
+    """Dropout rate p and Philox seed of the following forwards (p = 0: off)."""
+    _check(lib().gpt_attn_set_dropout(h, float(p), int(seed) & 0xFFFFFFFFFFFFFFFF),
+           "gpt_attn_set_dropout")
 
 
 def gpt_attn_destroy(h):

@@ -13,8 +13,9 @@
  *   y_m = merge_heads(att v)
  *   y   = y_m . W_proj + b_proj                    c_proj
  *
- * Dropout is the identity (dropout 0.0 in GPTConfig, page "nanoGPT global
- * flow walkthrough", section 2.1).
+ * Dropout is the identity by default (dropout 0.0 in GPTConfig, page
+ * "nanoGPT global flow walkthrough", section 2.1); gpt_attn_set_dropout
+ * switches on the training-time dropout.
  *
  * Conventions for every entry point:
  *   - Tensors are row-major and contiguous.  Weights are [in, out]
@@ -111,6 +112,24 @@ int gpt_attn_backward(gpt_attn_t h, const void *x, const void *W_attn,
                       const void *W_proj, const void *dY, void *dx,
                       void *dW_attn, void *db_attn, void *dW_proj,
                       void *db_proj, int B, int T, void *stream);
+
+/* Dropout for the following forwards on this handle (training): nn.Dropout
+ * on the attention weights after the softmax and on the c_proj output, rate
+ * p = config.dropout (page "nanoGPT architecture explained step by step",
+ * section 3, attn_dropout and resid_dropout).  p = 0 (the default) is the
+ * identity.  Masks come from the Philox4x32-10 counter-based generator
+ * (Salmon et al., SC 2011) keyed by seed (low word, high word): attention
+ * weight (b, h, query i, key j) uses counter (j/4, i, b*n_head + h, 1) and
+ * output word j%4; c_proj output (row m = b*T + t, column n) uses counter
+ * (n/4, m, 0, 2) and word n%4; an element is dropped iff its word is below
+ * floor(p * 2^32), kept elements are scaled by 1/(1-p).  The softmax row is
+ * normalised over all visible keys before dropping.  A forward with
+ * save_for_backward records p and seed; a backward of such a forward is
+ * UNSUPPORTED in this version.  Callers change the seed between steps.
+ * Applies to gpt_attn_forward and gpt_attn_block_forward (bf16), not to
+ * decoding.  Errors: INVALID_ARG (NULL handle, p < 0, p >= 1 or NaN),
+ * UNSUPPORTED (p > 0 on an fp32 handle). */
+int gpt_attn_set_dropout(gpt_attn_t h, float p, unsigned long long seed);
 
 /* Release the handle and its workspace (waits for the device first).
  * NULL is a no-op.  Returns OK or HIP. */

@@ -69,6 +69,9 @@ def _declare(lib):
     lib.oracle_dropout_keep_attn.argtypes = [i, i, i, i, i, ctypes.c_uint64, ctypes.c_uint32]
     lib.oracle_dropout_keep_resid.restype = i
     lib.oracle_dropout_keep_resid.argtypes = [ctypes.c_long, i, ctypes.c_uint64, ctypes.c_uint32]
+    lib.oracle_backward_dropout.restype = i
+    lib.oracle_backward_dropout.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, ctypes.c_double,
+                                            ctypes.c_uint64, dp, dp, dp, dp, dp, dp, dp, i, i]
     lib.oracle_forward_dropout.restype = i
     lib.oracle_forward_dropout.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, ctypes.c_double,
                                            ctypes.c_uint64, dp, dp, i, i]
@@ -145,18 +148,20 @@ def forward(x, W_attn, b_attn, W_proj, b_proj, n_head, *, want=("y",),
     return {k: v for k, v in out.items() if k in want}
 
 
-_STORE_BITS = {"qkv": 1, "ym": 2, "dym": 4, "dqkv": 8}
+_STORE_BITS = {"qkv": 1, "ym": 2, "dym": 4, "dqkv": 8, "dyd": 16}
 
 
 def backward(x, W_attn, b_attn, W_proj, b_proj, dY, n_head, *, want_inter=False,
-             store_bf16=(), nthreads=None, lib=None):
+             store_bf16=(), nthreads=None, lib=None, p=0.0, seed=0):
     """Exact fp64 gradient of the layer for upstream gradient dY [B,T,C].
 
     Returns dict with dx, dW_attn, dW_proj and (when the layer has biases)
     db_attn, db_proj; with ``want_inter`` also dqkv [B,T,3C] and dym.
-    ``store_bf16`` may name "qkv", "ym", "dym", "dqkv": those stored tensors
-    are rounded to bfloat16 and the gradients are the exact chain rule
-    through the rounded values."""
+    ``store_bf16`` may name "qkv", "ym", "dym", "dqkv" (and, with dropout,
+    "dyd": the masked, rescaled upstream gradient of the c_proj output):
+    those stored tensors are rounded to bfloat16 and the gradients are the
+    exact chain rule through the rounded values.  ``p`` > 0: gradient of the
+    forward with dropout rate p and generator ``seed`` (forward_dropout)."""
     lib = lib or load()
     x = _f64(x)
     B, T, C = x.shape
@@ -172,14 +177,16 @@ def backward(x, W_attn, b_attn, W_proj, b_proj, dY, n_head, *, want_inter=False,
     if want_inter:
         out["dqkv"] = np.empty((B, T, 3 * C))
         out["dym"] = np.empty((B, T, C))
-    rc = lib.oracle_backward(B, T, C, H, _ptr(x), _ptr(W_attn), _ptr(b_attn),
-                             _ptr(W_proj), _ptr(b_proj), _ptr(dY),
-                             _ptr(out["dx"]), _ptr(out["dW_attn"]),
-                             _ptr(out.get("db_attn")), _ptr(out["dW_proj"]),
-                             _ptr(out.get("db_proj")), _ptr(out.get("dqkv")),
-                             _ptr(out.get("dym")),
-                             sum(_STORE_BITS[k] for k in set(store_bf16)),
-                             int(nthreads or default_threads()))
+    bits = sum(_STORE_BITS[k] for k in set(store_bf16))
+    args = (_ptr(out["dx"]), _ptr(out["dW_attn"]), _ptr(out.get("db_attn")),
+            _ptr(out["dW_proj"]), _ptr(out.get("db_proj")), _ptr(out.get("dqkv")),
+            _ptr(out.get("dym")), bits, int(nthreads or default_threads()))
+    common = (B, T, C, H, _ptr(x), _ptr(W_attn), _ptr(b_attn), _ptr(W_proj), _ptr(b_proj),
+              _ptr(dY))
+    if p > 0:
+        rc = lib.oracle_backward_dropout(*common, float(p), int(seed), *args)
+    else:
+        rc = lib.oracle_backward(*common, *args)
     if rc != 0:
         raise ValueError("oracle_backward failed (bad shape or out of memory)")
     return out

@@ -312,7 +312,12 @@ typedef struct {
   int B, T, C, H;
   const double *qkv, *dym;
   double *dqkv;
+  double p;      /* dropout rate of the attention weights (0: none) */
+  uint64_t seed;
 } attn_bwd_ctx;
+
+int oracle_dropout_keep_attn(int b, int h, int H, int i, int j, uint64_t seed, uint32_t thresh);
+uint32_t oracle_dropout_threshold(double p);
 
 static void attn_bwd_head(void *vctx, long item, double *scratch) {
   const attn_bwd_ctx *c = (const attn_bwd_ctx *)vctx;
@@ -322,6 +327,10 @@ static void attn_bwd_head(void *vctx, long item, double *scratch) {
   const double scale = 1.0 / sqrt((double)hs);
   double *p = scratch;       /* [T] probabilities of row i */
   double *dp = scratch + T;  /* [T] dL/dp_ij               */
+  /* dropout: weight p_ij enters o_i as p_ij z_ij with z_ij = 1/(1-p) if
+   * kept, 0 if dropped (z = 1 without dropout) */
+  const double keep_scale = c->p > 0.0 ? 1.0 / (1.0 - c->p) : 1.0;
+  const uint32_t thresh = c->p > 0.0 ? oracle_dropout_threshold(c->p) : 0u;
   /* zero this head's dq, dk, dv columns */
   for (int t = 0; t < T; ++t) {
     double *r = c->dqkv + ((size_t)b * T + t) * ld + (size_t)h * hs;
@@ -336,13 +345,16 @@ static void attn_bwd_head(void *vctx, long item, double *scratch) {
     for (int j = 0; j <= i; ++j) {
       const double *vj = c->qkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;
       double *dvj = c->dqkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;
+      const double z =
+          (c->p > 0.0 && !oracle_dropout_keep_attn(b, h, H, i, j, c->seed, thresh)) ? 0.0
+                                                                                    : keep_scale;
       double s = 0.0;
       for (int d = 0; d < hs; ++d) {
         s += dO[d] * vj[d];
-        dvj[d] += p[j] * dO[d];
+        dvj[d] += p[j] * z * dO[d];
       }
-      dp[j] = s;
-      rowdot += p[j] * s;
+      dp[j] = s * z;
+      rowdot += p[j] * dp[j];
     }
     /* softmax Jacobian: ds_ij = p_ij (dp_ij - sum_j' p_ij' dp_ij');
      * scores s_ij = scale q_i . k_j  =>  dq_i += scale ds_ij k_j,
@@ -369,38 +381,62 @@ static void attn_bwd_head(void *vctx, long item, double *scratch) {
  * them: bit 0 qkv and bit 1 the merged heads (as in oracle_forward), bit 2
  * the gradient of the merged heads, bit 3 the gradient of qkv; every
  * gradient is then the exact chain rule through those stored values. */
-int oracle_backward(int B, int T, int C, int H, const double *x,
-                    const double *W_attn, const double *b_attn,
-                    const double *W_proj, const double *b_proj,
-                    const double *dY, double *dx, double *dW_attn,
-                    double *db_attn, double *dW_proj, double *db_proj,
-                    double *dqkv_out, double *dym_out, int store_bf16,
-                    int nthreads) {
+static int forward_dropout_impl(int B, int T, int C, int H, const double *x,
+                                const double *W_attn, const double *b_attn,
+                                const double *W_proj, const double *b_proj, double p,
+                                uint64_t seed, double *y, double *qkv, double *ym,
+                                int store_bf16, int nthreads);
+int oracle_dropout_keep_resid(long m, int n, uint64_t seed, uint32_t thresh);
+
+static int backward_impl(int B, int T, int C, int H, const double *x, const double *W_attn,
+                         const double *b_attn, const double *W_proj, const double *b_proj,
+                         const double *dY, double p_drop, uint64_t seed, double *dx,
+                         double *dW_attn, double *db_attn, double *dW_proj, double *db_proj,
+                         double *dqkv_out, double *dym_out, int store_bf16, int nthreads) {
   if (B < 0 || T < 0 || C <= 0 || H <= 0 || C % H != 0) return -1;
   if (!x || !W_attn || !W_proj || !dY || !dx || !dW_attn || !dW_proj) return -1;
+  if (!(p_drop >= 0.0 && p_drop < 1.0)) return -1;
   const long M = (long)B * T;
   int rc = -1;
   double *qkv = (double *)malloc(((size_t)M * 3 * C + 1) * sizeof(double));
   double *ym = (double *)malloc(((size_t)M * C + 1) * sizeof(double));
   double *y = (double *)malloc(((size_t)M * C + 1) * sizeof(double));
+  double *dyd = (double *)malloc(((size_t)M * C + 1) * sizeof(double));
   double *dym = dym_out ? dym_out : (double *)malloc(((size_t)M * C + 1) * sizeof(double));
   double *dqkv = dqkv_out ? dqkv_out : (double *)malloc(((size_t)M * 3 * C + 1) * sizeof(double));
-  if (!qkv || !ym || !y || !dym || !dqkv) goto done;
-  if (oracle_forward(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, y, qkv, ym,
-                     NULL, NULL, store_bf16 & 3, nthreads))
-    goto done;
+  if (!qkv || !ym || !y || !dyd || !dym || !dqkv) goto done;
+  if (p_drop > 0.0) {
+    if (M > 0 && forward_dropout_impl(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, p_drop,
+                                      seed, y, qkv, ym, store_bf16 & 3, nthreads))
+      goto done;
+    /* resid_dropout: y = drop(ym . W_proj + b_proj)  =>  the c_proj
+     * gradients see dY z with z = 1/(1-p) (kept) or 0 (dropped) */
+    const uint32_t thresh = oracle_dropout_threshold(p_drop);
+    const double ks = 1.0 / (1.0 - p_drop);
+    for (long m = 0; m < M; ++m)
+      for (int n = 0; n < C; ++n)
+        dyd[(size_t)m * C + n] = oracle_dropout_keep_resid(m, n, seed, thresh)
+                                     ? dY[(size_t)m * C + n] * ks
+                                     : 0.0;
+    if (store_bf16 & 16) round_all(dyd, (size_t)M * C);
+  } else {
+    if (oracle_forward(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, y, qkv, ym,
+                       NULL, NULL, store_bf16 & 3, nthreads))
+      goto done;
+    memcpy(dyd, dY, (size_t)M * C * sizeof(double));
+  }
   /* c_proj: y = ym . W_proj + b_proj */
-  if (db_proj) bias_grad((int)M, C, dY, db_proj);
+  if (db_proj) bias_grad((int)M, C, dyd, db_proj);
   {
-    wgrad_ctx w = {(int)M, C, C, ym, dY, dW_proj};
+    wgrad_ctx w = {(int)M, C, C, ym, dyd, dW_proj};
     if (parallel_for(C, nthreads, wgrad_row, &w, 0)) goto done;
-    dgrad_ctx g = {C, C, dY, W_proj, dym};
+    dgrad_ctx g = {C, C, dyd, W_proj, dym};
     if (parallel_for(M, nthreads, dgrad_row, &g, 0)) goto done;
   }
   if (store_bf16 & 4) round_all(dym, (size_t)M * C);
   /* attention core */
   {
-    attn_bwd_ctx a = {B, T, C, H, qkv, dym, dqkv};
+    attn_bwd_ctx a = {B, T, C, H, qkv, dym, dqkv, p_drop, seed};
     if (parallel_for((long)B * H, nthreads, attn_bwd_head, &a, (size_t)2 * T + 2))
       goto done;
   }
@@ -419,9 +455,36 @@ done:
   free(qkv);
   free(ym);
   free(y);
+  free(dyd);
   if (!dym_out) free(dym);
   if (!dqkv_out) free(dqkv);
   return rc;
+}
+
+int oracle_backward(int B, int T, int C, int H, const double *x,
+                    const double *W_attn, const double *b_attn,
+                    const double *W_proj, const double *b_proj,
+                    const double *dY, double *dx, double *dW_attn,
+                    double *db_attn, double *dW_proj, double *db_proj,
+                    double *dqkv_out, double *dym_out, int store_bf16,
+                    int nthreads) {
+  return backward_impl(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, dY, 0.0, 0, dx, dW_attn,
+                       db_attn, dW_proj, db_proj, dqkv_out, dym_out, store_bf16, nthreads);
+}
+
+/* Exact gradient of the forward with dropout rate p and generator seed
+ * (oracle_forward_dropout): the same masks scale the gradients that flow
+ * through the dropped weights and outputs.  store_bf16 bit 4 (value 16)
+ * additionally rounds the masked, rescaled upstream gradient of the c_proj
+ * output, which a bf16 path stores. */
+int oracle_backward_dropout(int B, int T, int C, int H, const double *x, const double *W_attn,
+                            const double *b_attn, const double *W_proj, const double *b_proj,
+                            const double *dY, double p, uint64_t seed, double *dx,
+                            double *dW_attn, double *db_attn, double *dW_proj,
+                            double *db_proj, double *dqkv_out, double *dym_out, int store_bf16,
+                            int nthreads) {
+  return backward_impl(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, dY, p, seed, dx, dW_attn,
+                       db_attn, dW_proj, db_proj, dqkv_out, dym_out, store_bf16, nthreads);
 }
 
 /* ------------------------------------------------------------------ */
@@ -605,6 +668,30 @@ static void drop_attn_head(void *vctx, long item, double *p) {
  * otherwise as oracle_forward (ym_out optional; store_bf16 bits 0 / 1 round
  * qkv / merged heads).  p = 0 keeps everything (same result as
  * oracle_forward). */
+static int forward_dropout_impl(int B, int T, int C, int H, const double *x,
+                                const double *W_attn, const double *b_attn,
+                                const double *W_proj, const double *b_proj, double p,
+                                uint64_t seed, double *y, double *qkv, double *ym,
+                                int store_bf16, int nthreads) {
+  const long M = (long)B * T;
+  const uint32_t thresh = oracle_dropout_threshold(p);
+  if (linear((int)M, C, 3 * C, x, W_attn, b_attn, qkv, nthreads)) return -1;
+  if (store_bf16 & 1) round_all(qkv, (size_t)M * 3 * C);
+  {
+    drop_attn_ctx a = {B, T, C, H, qkv, ym, p, seed, thresh};
+    if (parallel_for((long)B * H, nthreads, drop_attn_head, &a, (size_t)T)) return -1;
+  }
+  if (store_bf16 & 2) round_all(ym, (size_t)M * C);
+  if (linear((int)M, C, C, ym, W_proj, b_proj, y, nthreads)) return -1;
+  const double keep_scale = 1.0 / (1.0 - p);
+  for (long m = 0; m < M; ++m)
+    for (int n = 0; n < C; ++n)
+      y[(size_t)m * C + n] = oracle_dropout_keep_resid(m, n, seed, thresh)
+                                 ? y[(size_t)m * C + n] * keep_scale
+                                 : 0.0;
+  return 0;
+}
+
 int oracle_forward_dropout(int B, int T, int C, int H, const double *x, const double *W_attn,
                            const double *b_attn, const double *W_proj, const double *b_proj,
                            double p, uint64_t seed, double *y, double *ym_out, int store_bf16,
@@ -613,29 +700,12 @@ int oracle_forward_dropout(int B, int T, int C, int H, const double *x, const do
   if (!x || !W_attn || !W_proj || !y || !(p >= 0.0 && p < 1.0)) return -1;
   const long M = (long)B * T;
   if (M == 0) return 0;
-  const uint32_t thresh = oracle_dropout_threshold(p);
   double *qkv = (double *)malloc((size_t)M * 3 * C * sizeof(double));
   double *ym = ym_out ? ym_out : (double *)malloc((size_t)M * C * sizeof(double));
   int rc = -1;
-  if (!qkv || !ym) goto done;
-  if (linear((int)M, C, 3 * C, x, W_attn, b_attn, qkv, nthreads)) goto done;
-  if (store_bf16 & 1) round_all(qkv, (size_t)M * 3 * C);
-  {
-    drop_attn_ctx a = {B, T, C, H, qkv, ym, p, seed, thresh};
-    if (parallel_for((long)B * H, nthreads, drop_attn_head, &a, (size_t)T)) goto done;
-  }
-  if (store_bf16 & 2) round_all(ym, (size_t)M * C);
-  if (linear((int)M, C, C, ym, W_proj, b_proj, y, nthreads)) goto done;
-  {
-    const double keep_scale = 1.0 / (1.0 - p);
-    for (long m = 0; m < M; ++m)
-      for (int n = 0; n < C; ++n)
-        y[(size_t)m * C + n] = oracle_dropout_keep_resid(m, n, seed, thresh)
-                                   ? y[(size_t)m * C + n] * keep_scale
-                                   : 0.0;
-  }
-  rc = 0;
-done:
+  if (qkv && ym)
+    rc = forward_dropout_impl(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, p, seed, y, qkv,
+                              ym, store_bf16, nthreads);
   free(qkv);
   if (!ym_out) free(ym);
   return rc;

@@ -87,3 +87,49 @@ def test_composition_on_a_tiny_case(p):
                                  p, seed, want_ym=True)
     np.testing.assert_allclose(got["ym"], ym, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(got["y"], y, rtol=1e-12, atol=1e-14)
+
+
+def test_backward_p_zero_is_the_plain_backward():
+    inp = make_inputs(2, 9, 16, 4, dtype="f32", seed=5, w_std=0.3, proj_std=0.3, with_dY=True)
+    a = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, 4)
+    b = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, 4,
+                        p=1e-300, seed=3)   # keeps every element; scale 1/(1-p) == 1.0
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_with_dropout_matches_finite_differences():
+    """L = sum(y * dY) with y the forward with dropout (masks fixed by the
+    seed, so L is smooth in every parameter): central differences in fp64
+    against the analytic gradient, on sampled entries of every tensor."""
+    B, T, C, H = 2, 7, 8, 2
+    p, seed = 0.4, 2024
+    inp = make_inputs(B, T, C, H, dtype="f32", seed=19, w_std=0.4, proj_std=0.4,
+                      b_attn_std=0.2, b_proj_std=0.2, with_dY=True)
+    args = {k: np.asarray(getattr(inp, k), np.float64)
+            for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj")}
+    dY = np.asarray(inp.dY, np.float64)
+
+    def loss(a):
+        y = oracle.forward_dropout(a["x"], a["W_attn"], a["b_attn"], a["W_proj"], a["b_proj"],
+                                   H, p, seed)["y"]
+        return float(np.sum(y * dY))
+
+    g = oracle.backward(args["x"], args["W_attn"], args["b_attn"], args["W_proj"],
+                        args["b_proj"], dY, H, p=p, seed=seed)
+    names = {"x": "dx", "W_attn": "dW_attn", "b_attn": "db_attn", "W_proj": "dW_proj",
+             "b_proj": "db_proj"}
+    rng = np.random.default_rng(0)
+    eps = 1e-6
+    for k, gk in names.items():
+        flat = args[k].reshape(-1)
+        for idx in rng.choice(flat.size, size=min(24, flat.size), replace=False):
+            old = flat[idx]
+            flat[idx] = old + eps
+            lp = loss(args)
+            flat[idx] = old - eps
+            lm = loss(args)
+            flat[idx] = old
+            fd = (lp - lm) / (2 * eps)
+            an = g[gk].reshape(-1)[idx]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (k, idx, fd, an)

@@ -49,7 +49,7 @@ MUTANTS = [
     ("softmax grad without row term",
      [("const double ds = p[j] * (dp[j] - rowdot);", "const double ds = p[j] * dp[j];", 0)]),
     ("key grad sign", [("dkj[d] += scale * ds * qi[d];", "dkj[d] -= scale * ds * qi[d];", 0)]),
-    ("value grad wrong operand", [("dvj[d] += p[j] * dO[d];", "dvj[d] += p[j] * qi[d];", 0)]),
+    ("value grad wrong operand", [("dvj[d] += p[j] * z * dO[d];", "dvj[d] += p[j] * z * qi[d];", 0)]),
     ("query grad without scale", [("dqi[d] += scale * ds * kj[d];", "dqi[d] += ds * kj[d];", 0)]),
     ("bias grad drops last row",
      [("db[n] += dout[(size_t)m * N + n];",
@@ -75,6 +75,10 @@ MUTANTS = [
     ("residual dropout not rescaled", [("? y[(size_t)m * C + n] * keep_scale",
                                         "? y[(size_t)m * C + n]", 0)]),
     ("dropout word index", [("return w[c0 & 3] >= thresh;", "return w[0] >= thresh;", 0)]),
+    ("dropout backward: value grad unmasked", [("dvj[d] += p[j] * z * dO[d];",
+                                                "dvj[d] += p[j] * dO[d];", 0)]),
+    ("dropout backward: weight grad unmasked", [("dp[j] = s * z;", "dp[j] = s;", 0)]),
+    ("dropout backward: output grad unmasked", [("? dY[(size_t)m * C + n] * ks", "? dY[(size_t)m * C + n]", 0)]),
     ("input grad with untransposed square weight",
      [("s += g[n] * w[n];",
        "s += g[n] * (c->K == c->N ? c->W[(size_t)n * c->N + k] : w[n]);", 0)]),
@@ -154,6 +158,25 @@ def _pins(lib):
                                  lib=lib)["y"]
     if not np.allclose(got, yd, rtol=1e-12, atol=1e-14):
         failed.append("dropout composition")
+    # dropout backward against central differences of the dropout forward
+    dY = np.random.default_rng(5).standard_normal((1, 5, 8))
+    A = {k: np.array(getattr(di, k), np.float64) for k in ("x", "W_attn", "W_proj")}
+    gd = oracle.backward(A["x"], A["W_attn"], di.b_attn, A["W_proj"], di.b_proj, dY, 2,
+                         p=pd, seed=sd, lib=lib)
+    for k, gk in (("x", "dx"), ("W_attn", "dW_attn"), ("W_proj", "dW_proj")):
+        flat = A[k].reshape(-1)
+        for idx in (0, flat.size // 3, flat.size - 1):
+            old = flat[idx]
+            vals = []
+            for e in (1e-6, -1e-6):
+                flat[idx] = old + e
+                yy = oracle.forward_dropout(A["x"], A["W_attn"], di.b_attn, A["W_proj"],
+                                            di.b_proj, 2, pd, sd, lib=lib)["y"]
+                vals.append(float(np.sum(yy * dY)))
+            flat[idx] = old
+            fd = (vals[0] - vals[1]) / 2e-6
+            if abs(fd - gd[gk].reshape(-1)[idx]) > 1e-6 * max(1.0, abs(fd)):
+                failed.append("dropout backward fd")
     # brute force forward, incl. P and the log-sum-exp
     for (B, T, C, H, bias) in ((2, 5, 8, 2, True), (2, 6, 16, 4, False)):
         inp = make_inputs(B, T, C, H, bias=bias, dtype="f32", seed=T, w_std=0.5,
