@@ -19,10 +19,15 @@
 //
 // The gradients land in dqkv [B][T][3C] (columns: q block, k block, v block;
 // head h at h*hs within each), the layout the c_attn backward GEMMs read.
+//
+// With dropout on the weights (DROP; philox.cuh) o_i = sum_j p_ij z_ij v_j,
+// z_ij = 1/(1-p) for kept and 0 for dropped weights: dv_j sums p_ij z_ij dO_i,
+// dP_ij = z_ij dO_i . v_j, and D_i = dO_i . o_i is unchanged.
 #pragma once
 
 #include "common.cuh"
 #include "gemm.cuh"
+#include "philox.cuh"
 
 namespace gpt_attn {
 
@@ -48,6 +53,30 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T_* __restrict__ 
   D[((size_t)b * H + h) * T + t] = s;
 }
 
+// ------------------------------------------------------ output dropout
+// dYd[m][n] = dY[m][n] * z_mn (z = 1/(1-p) kept, 0 dropped; the c_proj
+// output mask of philox.cuh), one thread per 4 columns.
+__global__ __launch_bounds__(256) void dropout_grad_kernel(const bf16_t* __restrict__ dY,
+                                                           bf16_t* __restrict__ dYd, long M,
+                                                           int C, DropParams drop) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;  // group of 4 columns
+  const int per = C / 4;
+  if (i >= M * per) return;
+  const long m = i / per;
+  const int n = (int)(i - m * per) * 4;
+  const uint4 w =
+      philox4x32_10(make_uint4((uint32_t)n >> 2, (uint32_t)m, 0u, 2u), drop.k0, drop.k1);
+  const uint2 u = *reinterpret_cast<const uint2*>(dY + m * C + n);
+  const float z0 = w.x >= drop.thresh ? drop.scale : 0.f;
+  const float z1 = w.y >= drop.thresh ? drop.scale : 0.f;
+  const float z2 = w.z >= drop.thresh ? drop.scale : 0.f;
+  const float z3 = w.w >= drop.thresh ? drop.scale : 0.f;
+  uint2 o;
+  o.x = pack_bf16x2(bf2f(u.x & 0xffff) * z0, bf2f(u.x >> 16) * z1);
+  o.y = pack_bf16x2(bf2f(u.y & 0xffff) * z2, bf2f(u.y >> 16) * z3);
+  *reinterpret_cast<uint2*>(dYd + m * C + n) = o;
+}
+
 // ========================================================= bf16, dK / dV
 // One block = 4 waves = 128 keys of one (b, h); wave w owns 32 keys and
 // keeps them (as MFMA B operands) in registers.  The block walks the query
@@ -62,12 +91,12 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T_* __restrict__ 
 constexpr int kBwdBK = 128;  // keys per block (dK/dV kernel)
 constexpr int kBwdBQ = 64;   // queries per tile (dK/dV kernel)
 
-template <int HS>
+template <int HS, bool DROP = false>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
     const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg,
     const bf16_t* __restrict__ Vg, const bf16_t* __restrict__ dOg,
     const float* __restrict__ lse, const float* __restrict__ Dg, bf16_t* __restrict__ dqkv,
-    int H, int T, float scale, float scale_log2) {
+    int H, int T, float scale, float scale_log2, DropParams drop = {}) {
   constexpr int P1 = HS + 8;       // [q][d] pitch
   constexpr int P2 = kBwdBQ + 4;   // [d][q] pitch
   __shared__ __align__(16) bf16_t Qs[kBwdBQ * P1];
@@ -187,8 +216,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
           const int q = i0 + ql;
           float p = __builtin_amdgcn_exp2f(s[qh][r] * scale_log2 - Ls[ql]);
           if (mykey > q || q >= T) p = 0.f;
-          s[qh][r] = p;
-          dp[qh][r] = p * (dp[qh][r] - Ds[ql]);
+          if constexpr (DROP) {
+            // weight (query q, key mykey): word mykey % 4 of counter
+            // (mykey / 4, q, bh, 1)
+            const uint4 w = philox4x32_10(
+                make_uint4((uint32_t)mykey >> 2, (uint32_t)q, (uint32_t)bh, 1u), drop.k0,
+                drop.k1);
+            const uint32_t k = mykey & 3;
+            const uint32_t wd = k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
+            const float z = wd >= drop.thresh ? drop.scale : 0.f;
+            s[qh][r] = p * z;
+            dp[qh][r] = p * (dp[qh][r] * z - Ds[ql]);
+          } else {
+            s[qh][r] = p;
+            dp[qh][r] = p * (dp[qh][r] - Ds[ql]);
+          }
         }
       }
       // dV^T += dO^T P ;  dK^T += Q^T dS   (k index = queries, permuted order)
@@ -247,12 +289,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_bf16_kernel(
 //   S^T = K Q^T, dP^T = V dO^T (keys on rows, lane = query),
 //   P^T = exp2(S^T*scale*log2e - L*log2e), dS^T = P^T (dP^T - D),
 //   dQ^T += K^T dS^T.
-template <int HS>
+template <int HS, bool DROP = false>
 __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
     const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg,
     const bf16_t* __restrict__ Vg, const bf16_t* __restrict__ dOg,
     const float* __restrict__ lse, const float* __restrict__ Dg, bf16_t* __restrict__ dqkv,
-    int H, int T, float scale, float scale_log2) {
+    int H, int T, float scale, float scale_log2, DropParams drop = {}) {
   constexpr int BQ = 128, BK = 64;
   constexpr int P1 = HS + 8;   // [key][d] pitch
   constexpr int P2 = BK + 4;   // [d][key] pitch
@@ -344,12 +386,27 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_bf16_kernel(
           s[kt] = mfma32(ka, qf[kk], s[kt]);
           dp[kt] = mfma32(va, gf[kk], dp[kt]);
         }
+        uint4 wz[4];  // DROP: words of the 4 consecutive keys of each register group
+        if constexpr (DROP) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            wz[g] = philox4x32_10(
+                make_uint4((uint32_t)(j0 + kt * 32 + 8 * g + 4 * hi) >> 2, (uint32_t)myq,
+                           (uint32_t)bh, 1u),
+                drop.k0, drop.k1);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + kt * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
           float p = __builtin_amdgcn_exp2f(s[kt][r] * scale_log2 - L2);
           if (key > myq || myq >= T) p = 0.f;
-          dp[kt][r] = p * (dp[kt][r] - Dq);
+          if constexpr (DROP) {
+            const uint4 w = wz[r >> 2];
+            const uint32_t wd = (r & 3) == 0 ? w.x : (r & 3) == 1 ? w.y : (r & 3) == 2 ? w.z : w.w;
+            dp[kt][r] = p * (dp[kt][r] * (wd >= drop.thresh ? drop.scale : 0.f) - Dq);
+          } else {
+            dp[kt][r] = p * (dp[kt][r] - Dq);
+          }
         }
       }
 #pragma unroll

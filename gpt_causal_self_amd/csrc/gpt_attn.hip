@@ -208,7 +208,6 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
       (db_attn && !aligned16(db_attn)) || (db_proj && !aligned16(db_proj)))
     return GPT_ATTN_ERR_ALIGN;
   if (!h->saved || h->saved_B != B || h->saved_T != T) return GPT_ATTN_ERR_STATE;
-  if (h->saved_drop_p > 0.f) return GPT_ATTN_ERR_UNSUPPORTED;
 
   const int C = h->C, H = h->H, hs = h->hs;
   const int M = B * T, N3 = 3 * C;
@@ -260,6 +259,16 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     const bf16_t* o = (const bf16_t*)h->o;
     bf16_t* dym = (bf16_t*)h->dym;
     bf16_t* dqkv = (bf16_t*)h->dqkv;
+    // dropout of the saved forward: the c_proj gradients see the masked,
+    // rescaled upstream gradient (kept in the ln_1 buffer, unused here)
+    const bool drop = h->saved_drop_p > 0.f;
+    const DropParams dp = make_drop(h->saved_drop_p, h->saved_drop_seed);
+    if (drop) {
+      const long groups = (long)M * (C / 4);
+      hipLaunchKernelGGL(dropout_grad_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256),
+                         0, st, (const bf16_t*)dY, (bf16_t*)h->ln, (long)M, C, dp);
+      dY = h->ln;
+    }
     // ---- c_proj: dym = dY W_proj^T ; dW_proj = ym^T dY ; db_proj = colsum(dY)
     Epi2RowMajor e_dym{dym, C, nullptr};
     launch_gemm2<GA_DGRAD_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M, C,
@@ -287,17 +296,31 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     if (hs == 64) {
       hipLaunchKernelGGL((attn_delta_kernel<64, bf16_t>), dgrid, dim3(256), 0, st, dym, o,
                          h->delta, B, H, T);
-      hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, kgrid, dim3(256), 0, st, q, k, v, dym,
-                         h->lse, h->delta, dqkv, H, T, scale, scale_log2);
-      hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<64>, qgrid, dim3(256), 0, st, q, k, v, dym,
-                         h->lse, h->delta, dqkv, H, T, scale, scale_log2);
+      if (drop) {
+        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<64, true>), kgrid, dim3(256), 0, st, q, k,
+                           v, dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
+        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<64, true>), qgrid, dim3(256), 0, st, q, k, v,
+                           dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
+      } else {
+        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<64>), kgrid, dim3(256), 0, st, q, k, v,
+                           dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, DropParams{});
+        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<64>), qgrid, dim3(256), 0, st, q, k, v, dym,
+                           h->lse, h->delta, dqkv, H, T, scale, scale_log2, DropParams{});
+      }
     } else {
       hipLaunchKernelGGL((attn_delta_kernel<32, bf16_t>), dgrid, dim3(256), 0, st, dym, o,
                          h->delta, B, H, T);
-      hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<32>, kgrid, dim3(256), 0, st, q, k, v, dym,
-                         h->lse, h->delta, dqkv, H, T, scale, scale_log2);
-      hipLaunchKernelGGL(attn_bwd_dq_bf16_kernel<32>, qgrid, dim3(256), 0, st, q, k, v, dym,
-                         h->lse, h->delta, dqkv, H, T, scale, scale_log2);
+      if (drop) {
+        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<32, true>), kgrid, dim3(256), 0, st, q, k,
+                           v, dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
+        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<32, true>), qgrid, dim3(256), 0, st, q, k, v,
+                           dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
+      } else {
+        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<32>), kgrid, dim3(256), 0, st, q, k, v,
+                           dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, DropParams{});
+        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<32>), qgrid, dim3(256), 0, st, q, k, v, dym,
+                           h->lse, h->delta, dqkv, H, T, scale, scale_log2, DropParams{});
+      }
     }
     mark(h, 6, st);
     // ---- c_attn: dx = dqkv W_attn^T ; dW_attn = x^T dqkv ; db_attn = colsum(dqkv)

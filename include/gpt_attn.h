@@ -124,8 +124,10 @@ int gpt_attn_backward(gpt_attn_t h, const void *x, const void *W_attn,
  * (n/4, m, 0, 2) and word n%4; an element is dropped iff its word is below
  * floor(p * 2^32), kept elements are scaled by 1/(1-p).  The softmax row is
  * normalised over all visible keys before dropping.  A forward with
- * save_for_backward records p and seed; a backward of such a forward is
- * UNSUPPORTED in this version.  Callers change the seed between steps.
+ * save_for_backward records p and seed, and gpt_attn_backward then returns
+ * the exact gradient through the same masks (the upstream gradient of the
+ * c_proj output is masked, rescaled and stored in bf16 before the c_proj
+ * gradients).  Callers change the seed between steps.
  * Applies to gpt_attn_forward and gpt_attn_block_forward (bf16), not to
  * decoding.  Errors: INVALID_ARG (NULL handle, p < 0, p >= 1 or NaN),
  * UNSUPPORTED (p > 0 on an fp32 handle). */

@@ -12,7 +12,14 @@ standard deviation at most sigma = eps * sqrt(sum_r a_r^2 b_r^2), and the
 gate is the stated bf16 tolerance widened by six such sigmas:
     |g - r| <= 2e-2 + 1e-2 |r| + 6 sigma.
 A normwise gate ||g - r|| / ||r|| <= 1e-2 against the exact oracle holds on
-top of it."""
+top of it.
+
+One correlation is added explicitly.  The columns of the value block of dqkv
+sum to the column sums of dO, the stored gradient of the merged heads
+(sum_j dv_j = sum_i dO_i sum_j p_ij and every softmax row sums to one), so
+the bf16 rounding of each stored dO_i reaches db_attn's value block once per
+row with nothing averaging it out: that block's sigma also carries
+eps * sqrt(sum_i dO_id^2)."""
 from __future__ import annotations
 
 import numpy as np
@@ -29,9 +36,11 @@ def sigmas(inp, ref_inter):
     ym2 = ref_inter["ym"].reshape(-1, C) ** 2
     dY2 = inp.dY.reshape(-1, C).astype(np.float64) ** 2
     Wa2 = inp.W_attn.astype(np.float64) ** 2
+    db_attn2 = g2.sum(0)
+    db_attn2[2 * C:] += (ref_inter["dym"].reshape(-1, C) ** 2).sum(0)
     s = {"dx": np.sqrt(g2 @ Wa2.T).reshape(B, T, C),
          "dW_attn": np.sqrt(x2.T @ g2),
-         "db_attn": np.sqrt(g2.sum(0)),
+         "db_attn": np.sqrt(db_attn2),
          "dW_proj": np.sqrt(ym2.T @ dY2),
          "db_proj": np.sqrt(dY2.sum(0))}
     return {k: EPS * v for k, v in s.items()}

@@ -12,6 +12,9 @@ from __future__ import annotations
 import numpy as np
 import pytest
 
+import dataclasses
+
+import grad_gate
 import oracle
 from gpt_causal_self_amd import gpt_attn as ga
 from gpt_causal_self_amd.inputs import from_torch, make_inputs, make_ln_params, to_torch
@@ -128,12 +131,6 @@ def test_dropout_errors():
         with pytest.raises(ga.GptAttnError) as e:
             ga.gpt_attn_set_dropout(layer.h, bad, 0)
         assert e.value.code == ga.ERR_INVALID_ARG
-    inp = _inputs(1, 16, 128, 4, seed=1)
-    _fwd(inp, 0.1, 3, layer=layer, save=True)
-    d = {k: to_torch(getattr(inp, k), "bf16", "cuda") for k in ("x", "W_attn", "W_proj")}
-    with pytest.raises(ga.GptAttnError) as e:
-        layer.backward(d["x"], d["W_attn"], d["W_proj"], torch.ones_like(d["x"]))
-    assert e.value.code == ga.ERR_UNSUPPORTED
     layer.close()
     f32 = ga.Layer(128, 4, 1, 16, "f32")
     with pytest.raises(ga.GptAttnError) as e:
@@ -141,3 +138,32 @@ def test_dropout_errors():
     assert e.value.code == ga.ERR_UNSUPPORTED
     ga.gpt_attn_set_dropout(f32.h, 0.0, 0)        # switching off is always allowed
     f32.close()
+
+
+@pytest.mark.parametrize("B,T,C,H,p,seed", [(2, 70, 256, 4, 0.1, 31), (1, 129, 128, 4, 0.5, 32),
+                                            (2, 1024, 768, 12, 0.1, 33)])
+def test_dropout_backward(B, T, C, H, p, seed):
+    """Gradients of a dropout forward against the oracle's exact gradient
+    through the same masks, with the bf16 gradient gate; its rounding-noise
+    sigmas use |dY| / (1 - p), a bound on the masked upstream gradient."""
+    import torch
+    inp = make_inputs(B, T, C, H, dtype="bf16", seed=T + seed, with_dY=True)
+    layer = ga.Layer(C, H, B, T, "bf16")
+    d = {k: to_torch(getattr(inp, k), "bf16", "cuda")
+         for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj", "dY")}
+    ga.gpt_attn_set_dropout(layer.h, p, seed)
+    layer.forward(d["x"], d["W_attn"], d["b_attn"], d["W_proj"], d["b_proj"],
+                  save_for_backward=True)
+    g = {k: from_torch(v) for k, v in
+         layer.backward(d["x"], d["W_attn"], d["W_proj"], d["dY"]).items()}
+    torch.cuda.synchronize()
+    layer.close()
+    pf = float(np.float32(p))
+    r = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, H,
+                        want_inter=True, p=pf, seed=seed)
+    r["ym"] = oracle.forward_dropout(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, H,
+                                     pf, seed, want_ym=True)["ym"]
+    bound_inp = dataclasses.replace(inp, dY=inp.dY / (1 - pf))
+    sig = grad_gate.sigmas(bound_inp, r)
+    for k in ("dx", "dW_attn", "db_attn", "dW_proj", "db_proj"):
+        grad_gate.check(k, g[k], r[k], sig[k])
