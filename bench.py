@@ -295,8 +295,8 @@ def time_calls(fn, n, warm=3):
 def next_rows(n=50):
     """Timings of the pieces around the layer at the GPT-2 124M shape (B=12,
     T=1024, C=768, 12 heads, MLP width 3072): LayerNorm, the Pre-LN attention
-    half-block, one-token decode against a full KV cache, and the MLP
-    sublayer with its residual add."""
+    half-block, dropout (forward and training step), one-token decode
+    against a full KV cache, and the MLP sublayer with its residual add."""
     import torch
     from gpt_causal_self_amd import gpt_attn as ga
     from gpt_causal_self_amd.inputs import (WORKLOADS, make_inputs, make_ln_params,
@@ -329,6 +329,27 @@ def next_rows(n=50):
                               "ms": round(ms, 5),
                               "tflops": round(F_blk / (ms * 1e-3) / 1e12, 2),
                               "tokens_per_s": round(M / (ms * 1e-3), 1)}
+    # training-time dropout (p = 0.1): forward, and forward + backward
+    y = torch.empty_like(t["x"])
+    dY = torch.randn_like(t["x"].float()).to(torch.bfloat16)
+    grads = [torch.empty_like(t["x"]), torch.empty_like(t["W_attn"]), torch.empty_like(t["b_attn"]),
+             torch.empty_like(t["W_proj"]), torch.empty_like(t["b_proj"])]
+    ga.gpt_attn_set_dropout(layer.h, 0.1, 1234)
+    ms_f = time_calls(lambda: ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"],
+                                                  t["W_proj"], t["b_proj"], H, y), n)
+
+    def drop_step():
+        ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"], t["W_proj"],
+                            t["b_proj"], H, y, save_for_backward=True)
+        ga.gpt_attn_backward(layer.h, t["x"], t["W_attn"], t["W_proj"], dY, *grads)
+    ms_t = time_calls(drop_step, max(5, n // 5))
+    ga.gpt_attn_set_dropout(layer.h, 0.0, 0)
+    res["dropout"] = {"workload": f"dropout p=0.1 on the attention weights and the c_proj "
+                                  f"output, B={B} T={T} C={C} H={H} bf16",
+                      "forward_ms": round(ms_f, 5),
+                      "forward_tflops": round(F_blk / (ms_f * 1e-3) / 1e12, 2),
+                      "train_step_ms": round(ms_t, 5),
+                      "train_step_tflops": round(3 * F_blk / (ms_t * 1e-3) / 1e12, 2)}
     # one-token decode at the last position of a full 1024-token cache
     hs = C // H
     kc = torch.randn((B, H, T, hs), device=dev).to(torch.bfloat16)
