@@ -53,6 +53,94 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const T_* __restrict__ 
   D[((size_t)b * H + h) * T + t] = s;
 }
 
+// Sum over 4 (Q = 4) or 8 (Q = 8) consecutive lanes with DPP moves (quad
+// swaps, then the mirrored lane of the half-row); every lane of the group
+// ends with the group's total.
+template <int Q>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if (Q == 8)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v;
+}
+
+// D[bh][t] = dO[b][t][h*HS..] . O[b][t][h*HS..] for bf16: a thread takes 8
+// consecutive elements of a row (16-byte loads of both tensors), the HS/8
+// threads of one head meet with lane_group_sum.
+template <int HS>
+__global__ __launch_bounds__(256) void attn_delta_bf16_kernel(const bf16_t* __restrict__ dO,
+                                                              const bf16_t* __restrict__ O,
+                                                              float* __restrict__ D, int B, int H,
+                                                              int T) {
+  constexpr int Q = HS / 8;
+  const int C = H * HS, per = C / 8;
+  const long g = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)B * T * per;
+  const bool ok = g < total;
+  float s = 0.f;
+  long row = 0;
+  int c = 0;
+  if (ok) {
+    row = g / per;
+    c = (int)(g - row * per);
+    const uint4 a = *reinterpret_cast<const uint4*>(dO + row * C + 8 * c);
+    const uint4 o = *reinterpret_cast<const uint4*>(O + row * C + 8 * c);
+    const unsigned wa[4] = {a.x, a.y, a.z, a.w}, wo[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(bf2f(wa[e] & 0xffff), bf2f(wo[e] & 0xffff), s);
+      s = fmaf(bf2f(wa[e] >> 16), bf2f(wo[e] >> 16), s);
+    }
+  }
+  s = lane_group_sum<Q>(s);  // every lane takes part (groups never straddle the end)
+  if (ok && c % Q == 0) {
+    const int h = c / Q;
+    const long b = row / T, t = row - b * T;
+    D[((size_t)b * H + h) * T + t] = s;
+  }
+}
+
+// Column sums of a bf16 matrix: block (x, y) sums columns [64x, 64x + 64)
+// over rows [y * rows_per, (y + 1) * rows_per); 256 threads = 8 column groups
+// (16-byte loads of 8 columns) x 32 row slots, the slot sums meet in LDS in a
+// fixed order; part[y][n] receives the block's sums.  N % 8 == 0.
+__global__ __launch_bounds__(256) void colsum_bf16_kernel(const bf16_t* __restrict__ X, int M,
+                                                          int N, int ld, int rows_per,
+                                                          float* __restrict__ part) {
+  __shared__ float red[32][64];
+  const int tid = threadIdx.x, cg = tid & 7, slot = tid >> 3;
+  const int n = blockIdx.x * 64 + 8 * cg;
+  const int r0 = blockIdx.y * rows_per, r1 = min(M, r0 + rows_per);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (n < N) {
+    for (int r = r0 + slot; r < r1; r += 32 * 4) {
+      uint4 u[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        u[q] = r + 32 * q < r1 ? *reinterpret_cast<const uint4*>(X + (size_t)(r + 32 * q) * ld + n)
+                               : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const unsigned w[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf2f(w[e] & 0xffff);
+          acc[2 * e + 1] += bf2f(w[e] >> 16);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[slot][8 * cg + e] = acc[e];
+  __syncthreads();
+  if (tid < 64 && blockIdx.x * 64 + tid < N) {
+    float t = 0.f;
+    for (int sl = 0; sl < 32; ++sl) t += red[sl][tid];
+    part[(size_t)blockIdx.y * N + blockIdx.x * 64 + tid] = t;
+  }
+}
+
 // ------------------------------------------------------ output dropout
 // dYd[m][n] = dY[m][n] * z_mn (z = 1/(1-p) kept, 0 dropped; the c_proj
 // output mask of philox.cuh), one thread per 4 columns.
@@ -550,6 +638,24 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T_* __restric
 }
 
 // out[i] = sum_{s < S} part[s*stride + i] for i < n, in the output type.
+// out[i..i+3] = sum_k part[k][i..i+3] (n, stride multiples of 4; 16-byte
+// partial loads).
+__global__ __launch_bounds__(256) void reduce_partials4_bf16_kernel(
+    const float* __restrict__ part, int S, size_t n, size_t stride, bf16_t* __restrict__ out) {
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n;
+       i += (size_t)gridDim.x * 256 * 4) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < S; ++k) {
+      const float4 v = *reinterpret_cast<const float4*>(part + (size_t)k * stride + i);
+      s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    }
+    uint2 w;
+    w.x = pack_bf16x2(s.x, s.y);
+    w.y = pack_bf16x2(s.z, s.w);
+    *reinterpret_cast<uint2*>(out + i) = w;
+  }
+}
+
 template <class T_>
 __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ part,
                                                               int S, size_t n, size_t stride,

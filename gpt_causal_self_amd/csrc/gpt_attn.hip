@@ -6,6 +6,8 @@
 //             -> fused causal attention (merged-head output, optional LSE)
 //             -> c_proj GEMM (bias)
 //   backward: see attn_bwd.cuh / the launch sequence in gpt_attn_backward.
+#include <algorithm>
+
 #include "attn_bwd.cuh"
 #include "handle.cuh"
 #include "layer_fwd.cuh"
@@ -219,6 +221,9 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
   float* cpart = h->part + (size_t)kWgradSplits * C * N3;  // column-sum partials
   const int rows_per = (M + kColsumSplits - 1) / kColsumSplits;
   const int ncs = rows_per > 0 ? (M + rows_per - 1) / rows_per : 0;
+  // bf16 column sums: row slices of about 384 rows (12 rows per thread)
+  const int bcs = std::max(1, std::min(kColsumSplits, (M + 383) / 384));
+  const int brows = (M + bcs - 1) / bcs;
   auto splits_for = [](int tiles) {
     int s = (2 * 256 + tiles - 1) / tiles;
     return s < 1 ? 1 : (s > kWgradSplits ? kWgradSplits : s);
@@ -277,13 +282,13 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     const int s1 = splits_for(((C + 127) / 128) * ((C + 127) / 128));
     const int n1 = launch_gemm2<GA_WGRAD_TILE, false, false>(o, C, (const bf16_t*)dY, C, C, C, M,
                                                              e_wp, st, s1);
-    hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(rblocks), dim3(256), 0, st, part, n1,
+    hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, st, part, n1,
                        (size_t)C * C, (size_t)C * C, (bf16_t*)dW_proj);
     if (db_proj) {
-      hipLaunchKernelGGL(colsum_partial_kernel<bf16_t>, dim3((C + 255) / 256, ncs), dim3(256), 0,
-                         st, (const bf16_t*)dY, M, C, C, rows_per, cpart);
+      hipLaunchKernelGGL(colsum_bf16_kernel, dim3((C + 63) / 64, bcs), dim3(256), 0, st,
+                         (const bf16_t*)dY, M, C, C, brows, cpart);
       hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3((C + 255) / 256), dim3(256), 0, st,
-                         cpart, ncs, (size_t)C, (size_t)C, (bf16_t*)db_proj);
+                         cpart, bcs, (size_t)C, (size_t)C, (bf16_t*)db_proj);
     }
     mark(h, 5, st);
     // ---- attention core
@@ -293,9 +298,10 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     const bf16_t* q = qkv;
     const bf16_t* k = qkv + head_elems;
     const bf16_t* v = qkv + 2 * head_elems;
+    const dim3 vgrid((unsigned)(((long)M * (C / 8) + 255) / 256));
     if (hs == 64) {
-      hipLaunchKernelGGL((attn_delta_kernel<64, bf16_t>), dgrid, dim3(256), 0, st, dym, o,
-                         h->delta, B, H, T);
+      hipLaunchKernelGGL(attn_delta_bf16_kernel<64>, vgrid, dim3(256), 0, st, dym, o, h->delta,
+                         B, H, T);
       if (drop) {
         hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<64, true>), kgrid, dim3(256), 0, st, q, k,
                            v, dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
@@ -308,8 +314,8 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
                            h->lse, h->delta, dqkv, H, T, scale, scale_log2, DropParams{});
       }
     } else {
-      hipLaunchKernelGGL((attn_delta_kernel<32, bf16_t>), dgrid, dim3(256), 0, st, dym, o,
-                         h->delta, B, H, T);
+      hipLaunchKernelGGL(attn_delta_bf16_kernel<32>, vgrid, dim3(256), 0, st, dym, o, h->delta,
+                         B, H, T);
       if (drop) {
         hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<32, true>), kgrid, dim3(256), 0, st, q, k,
                            v, dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
@@ -331,13 +337,13 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     const int s2 = splits_for(((C + 127) / 128) * ((N3 + 127) / 128));
     const int n2 = launch_gemm2<GA_WGRAD_TILE, false, false>((const bf16_t*)x, C, dqkv, N3, C, N3,
                                                              M, e_wa, st, s2);
-    hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3(rblocks), dim3(256), 0, st, part, n2,
+    hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, st, part, n2,
                        (size_t)C * N3, (size_t)C * N3, (bf16_t*)dW_attn);
     if (db_attn) {
-      hipLaunchKernelGGL(colsum_partial_kernel<bf16_t>, dim3((N3 + 255) / 256, ncs), dim3(256), 0,
-                         st, dqkv, M, N3, N3, rows_per, cpart);
+      hipLaunchKernelGGL(colsum_bf16_kernel, dim3((N3 + 63) / 64, bcs), dim3(256), 0, st, dqkv, M,
+                         N3, N3, brows, cpart);
       hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3((N3 + 255) / 256), dim3(256), 0,
-                         st, cpart, ncs, (size_t)N3, (size_t)N3, (bf16_t*)db_attn);
+                         st, cpart, bcs, (size_t)N3, (size_t)N3, (bf16_t*)db_attn);
     }
   } else {
     const float* qkv = (const float*)h->qkv;
