@@ -1,0 +1,510 @@
+// attn_bwd2.cuh -- pipelined bf16 backward of the fused causal attention.
+//
+// Same gradient as attn_bwd.cuh (D_i = dO_i . o_i, P recomputed from the
+// log-sum-exp, dS = P (dP - D), dq_i = (1/sqrt(hs)) sum_j dS_ij k_j,
+// dk_j = (1/sqrt(hs)) sum_i dS_ij q_i, dv_j = sum_i p_ij dO_i; page "nanoGPT
+// global flow walkthrough", section 2.5 (B), differentiated by the chain
+// rule), organised like the forward kernel:
+//  * the tiles that stream (K and V for dQ; Q, dO and the rows' log-sum-exp
+//    and D for dK/dV) move global -> LDS with global_load_lds_dwordx4 into a
+//    two-stage ring, 16-byte chunks of each row XOR-swizzled by the row;
+//  * the operands that need the streamed tile transposed (K^T for dQ; Q^T
+//    and dO^T for dK/dV) are read with ds_read_b64_tr_b16 straight from the
+//    [row][d] tile, in the permuted row order of the probability registers;
+//  * the per-step body takes the stage it reads and the stage it fills as
+//    restrict pointers, so the LDS reads never wait for the loads in flight.
+// Every output element is written by exactly one lane (dQ: one block per
+// 128 queries; dK, dV: one block per 128 keys): no atomics, deterministic.
+#pragma once
+
+#include "attn_fwd.cuh"
+#include "common.cuh"
+#include "gemm2.cuh"
+#include "philox.cuh"
+
+namespace gpt_attn {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+
+// Padded per-row statistics for the dK/dV kernel: L2[bh][t] = lse * log2(e)
+// and D[bh][t] = dO_t . o_t, rows of Tpad = T rounded up to 64 (the padding
+// is never used: masked lanes select 0).  One thread per 8 elements of a row
+// of dO and O, the head's lanes summed with lane_group_sum.
+template <int HS>
+__global__ __launch_bounds__(256) void attn_bwd_rowstats_kernel(
+    const bf16_t* __restrict__ dO, const bf16_t* __restrict__ O, const float* __restrict__ lse,
+    float* __restrict__ Dpad, float* __restrict__ Lpad, int B, int H, int T, int Tpad) {
+  constexpr int Q = HS / 8;
+  const int C = H * HS, per = C / 8;
+  const long g = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)B * T * per;
+  const bool ok = g < total;
+  float s = 0.f;
+  long row = 0;
+  int c = 0;
+  if (ok) {
+    row = g / per;
+    c = (int)(g - row * per);
+    const uint4 a = *reinterpret_cast<const uint4*>(dO + row * C + 8 * c);
+    const uint4 o = *reinterpret_cast<const uint4*>(O + row * C + 8 * c);
+    const unsigned wa[4] = {a.x, a.y, a.z, a.w}, wo[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(bf2f(wa[e] & 0xffff), bf2f(wo[e] & 0xffff), s);
+      s = fmaf(bf2f(wa[e] >> 16), bf2f(wo[e] >> 16), s);
+    }
+  }
+  s = lane_group_sum<Q>(s);
+  if (ok && c % Q == 0) {
+    const int h = c / Q;
+    const long b = row / T, t = row - b * T;
+    const size_t bh = (size_t)b * H + h;
+    Dpad[bh * Tpad + t] = s;
+    Lpad[bh * Tpad + t] = lse[bh * T + t] * kLog2eB;
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+// One block = 4 waves = 128 queries of one (b, h); wave w owns 32 queries
+// (lane = query) and keeps q and dO of its query as MFMA B operands.  Per
+// 64-key tile: S^T = K Q^T and dP^T = V dO^T (keys on the MFMA rows),
+// P^T = exp2(S^T * scale * log2 e - L), dS^T = P^T (dP^T - D) (with DROP,
+// dP carries the keep factor z of the weight), dQ^T += K^T dS^T.
+template <int HS, bool DROP>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
+    const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg,
+    const bf16_t* __restrict__ Vg, const bf16_t* __restrict__ dOg,
+    const float* __restrict__ Lpad, const float* __restrict__ Dpad, bf16_t* __restrict__ dqkv,
+    int H, int T, int Tpad, float scale, float scale_log2, DropParams drop) {
+  static_assert(HS == 32 || HS == 64, "head size");
+  constexpr int BKV = 64;
+  constexpr int TILE = BKV * HS * 2;   // bytes of one K or V tile
+  constexpr int STAGE = 2 * TILE;
+  constexpr int RB = HS * 2;
+  constexpr int CPR = HS / 8;
+  constexpr int RPI = 64 / CPR;
+  constexpr int LPW = TILE / 1024 / 4;
+  __shared__ __align__(1024) char smem[2 * STAGE];
+
+  const int nqt = (T + 127) / 128;
+  const int bh = blockIdx.x;
+  const int qt = nqt - 1 - (int)blockIdx.y;  // heavy tiles first
+  const int b = bh / H, h = bh - b * H;
+  const int C = H * HS;
+  const size_t head = (size_t)bh * T * HS;
+  const bf16_t* Kh = Kg + head;
+  const bf16_t* Vh = Vg + head;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hi = lane >> 5;
+  const int q0 = qt * 128 + wid * 32;
+  const int myq = q0 + (lane & 31);
+
+  bf16x8 qf[HS / 16], gf[HS / 16];
+#pragma unroll
+  for (int kk = 0; kk < HS / 16; ++kk) {
+    if (myq < T) {
+      qf[kk] = *reinterpret_cast<const bf16x8*>(Qg + head + (size_t)myq * HS + 16 * kk + 8 * hi);
+      gf[kk] = *reinterpret_cast<const bf16x8*>(dOg + ((size_t)b * T + myq) * C + h * HS +
+                                                16 * kk + 8 * hi);
+    } else {
+      qf[kk] = bf16x8{};
+      gf[kk] = bf16x8{};
+    }
+  }
+  const float L2 = myq < T ? Lpad[(size_t)bh * Tpad + myq] : 0.f;
+  const float Dq = myq < T ? Dpad[(size_t)bh * Tpad + myq] : 0.f;
+  floatx16 dq[HS / 32];
+#pragma unroll
+  for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[dt][r] = 0.f;
+
+  // LDS offsets: row fragments (row kt*32 + lane%32, chunk 2kk + hi) and the
+  // transposing reads (row kb + 8t + 4(G/2) + s/4, column dt*32 + 16(G%2) +
+  // 4(s%4)), as in the forward kernel.
+  int koff[HS / 16];
+#pragma unroll
+  for (int kk = 0; kk < HS / 16; ++kk) {
+    const int row = lane & 31;
+    koff[kk] = row * RB + (((2 * kk + hi) ^ kv_swz<HS>(row)) << 4);
+  }
+  const int G = lane >> 4, s16 = lane & 15;
+  const int r0 = 4 * (G >> 1) + (s16 >> 2);
+  int toff[HS / 32];
+#pragma unroll
+  for (int dt = 0; dt < HS / 32; ++dt) {
+    const int d = dt * 32 + 16 * (G & 1) + 4 * (s16 & 3);
+    toff[dt] = r0 * RB + (((d >> 3) ^ kv_swz<HS>(r0)) << 4) + ((d >> 2) & 1) * 8;
+  }
+
+  const int kv_end = min(T, (qt + 1) * 128);
+  const int nkv = (kv_end + BKV - 1) / BKV;
+
+  auto issue = [&](char* dst, int j0) {
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int inst = wid * LPW + q;
+      const int row = inst * RPI + lane / CPR;
+      const int chunk = (lane % CPR) ^ kv_swz<HS>(row);
+      const int key = j0 + row;
+      const bool ok = key < T;
+      const bf16_t* gk = ok ? Kh + (size_t)key * HS + chunk * 8
+                            : reinterpret_cast<const bf16_t*>(&g_zero16);
+      const bf16_t* gv = ok ? Vh + (size_t)key * HS + chunk * 8
+                            : reinterpret_cast<const bf16_t*>(&g_zero16);
+      char* base = dst + inst * 1024;
+      __builtin_amdgcn_load_to_lds((void*)gk, GA_LDS(base), 16, 0, 0);
+      __builtin_amdgcn_load_to_lds((void*)gv, GA_LDS(base + TILE), 16, 0, 0);
+    }
+  };
+  issue(smem, 0);
+
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) const bf16x8 lds_b128;
+
+  auto tile = [&](auto mask_tag, const char* __restrict__ rd, char* __restrict__ wr, int jn,
+                  int j0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (jn >= 0) issue(wr, jn);
+    const lds_char* lbase = (const lds_char*)rd;
+    floatx16 sc[2], dp[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sc[kt][r] = 0.f;
+        dp[kt][r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < HS / 16; ++kk) {
+        const bf16x8 kf = *(lds_b128*)(lbase + koff[kk] + kt * 32 * RB);
+        const bf16x8 vf = *(lds_b128*)(lbase + TILE + koff[kk] + kt * 32 * RB);
+        sc[kt] = mfma32(kf, qf[kk], sc[kt]);
+        dp[kt] = mfma32(vf, gf[kk], dp[kt]);
+      }
+    }
+    // lane = query myq; register r of kt <-> key j0 + kt*32 + 8(r/4) + 4hi + r%4
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint4 w = make_uint4(0u, 0u, 0u, 0u);
+        if constexpr (DROP)
+          w = philox4x32_10(make_uint4((uint32_t)(j0 + kt * 32 + 8 * g + 4 * hi) >> 2,
+                                       (uint32_t)myq, (uint32_t)bh, 1u),
+                            drop.k0, drop.k1);
+        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][r], scale_log2, -L2));
+          float dpv = dp[kt][r];
+          if constexpr (DROP) dpv *= wd[e] >= drop.thresh ? drop.scale : 0.f;
+          float ds = p * (dpv - Dq);
+          if constexpr (MASK) {
+            const int key = j0 + kt * 32 + 8 * g + 4 * hi + e;
+            if (key > myq) ds = 0.f;
+          }
+          dp[kt][r] = ds;
+        }
+      }
+    }
+    // dQ^T += K^T dS^T; K^T by transposing reads in the key order of dS
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 sf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sf[e] = (__bf16)dp[kt][8 * u + e];
+        const int kb = kt * 32 + 16 * u;
+#pragma unroll
+        for (int dt = 0; dt < HS / 32; ++dt) {
+          v4i16 rv[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            rv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(lbase + toff[dt] + (kb + 8 * t) * RB));
+          typedef short v8i16 __attribute__((ext_vector_type(8)));
+          const v8i16 kv = {rv[0][0], rv[0][1], rv[0][2], rv[0][3],
+                            rv[1][0], rv[1][1], rv[1][2], rv[1][3]};
+          dq[dt] = mfma32(__builtin_bit_cast(bf16x8, kv), sf, dq[dt]);
+        }
+      }
+  };
+
+  const int n_full = min(nkv, (qt * 128) / BKV);
+  int it = 0;
+  for (; it < n_full; ++it) {
+    wait_vmcnt<0>();
+    bar_nofence();
+    const int jn = it + 1 < nkv ? (it + 1) * BKV : -1;
+    tile(std::integral_constant<bool, false>{}, smem + (it & 1) * STAGE,
+         smem + ((it + 1) & 1) * STAGE, jn, it * BKV);
+  }
+  for (; it < nkv; ++it) {
+    wait_vmcnt<0>();
+    bar_nofence();
+    const int jn = it + 1 < nkv ? (it + 1) * BKV : -1;
+    const int j0 = it * BKV;
+    char* wr = smem + ((it + 1) & 1) * STAGE;
+    if (j0 <= q0 + 31)
+      tile(std::integral_constant<bool, true>{}, smem + (it & 1) * STAGE, wr, jn, j0);
+    else if (jn >= 0)
+      issue(wr, jn);
+  }
+
+  if (myq < T) {
+    bf16_t* row = dqkv + ((size_t)b * T + myq) * 3 * C + (size_t)h * HS;
+#pragma unroll
+    for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * hi;
+        uint2 w;
+        w.x = pack_bf16x2(dq[dt][4 * g] * scale, dq[dt][4 * g + 1] * scale);
+        w.y = pack_bf16x2(dq[dt][4 * g + 2] * scale, dq[dt][4 * g + 3] * scale);
+        *reinterpret_cast<uint2*>(row + d0) = w;
+      }
+  }
+}
+
+// ------------------------------------------------------------- dK / dV
+// One block = 4 waves = 128 keys of one (b, h); wave w owns 32 keys (lane =
+// key) and keeps k and v of its key as MFMA B operands.  Per 64-query tile:
+// S = Q K^T and dP = dO V^T (queries on the MFMA rows), P = exp2(S * scale *
+// log2 e - L), dS = P (dP - D) (with DROP: P z for dV, dP z in dS),
+// dV^T += dO^T P and dK^T += Q^T dS.  Stage: Q tile, dO tile, then the 64
+// queries' L (log2 units) and D (fp32).
+template <int HS, bool DROP>
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
+    const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg,
+    const bf16_t* __restrict__ Vg, const bf16_t* __restrict__ dOg,
+    const float* __restrict__ Lpad, const float* __restrict__ Dpad, bf16_t* __restrict__ dqkv,
+    int H, int T, int Tpad, float scale, float scale_log2, DropParams drop) {
+  static_assert(HS == 32 || HS == 64, "head size");
+  constexpr int BQ = 64;
+  constexpr int TILE = BQ * HS * 2;    // bytes of one Q or dO tile
+  constexpr int STAGE = 2 * TILE + 512;
+  constexpr int RB = HS * 2;
+  constexpr int CPR = HS / 8;
+  constexpr int RPI = 64 / CPR;
+  constexpr int LPW = TILE / 1024 / 4;
+  __shared__ __align__(1024) char smem[2 * STAGE];
+
+  const int bh = blockIdx.x;
+  const int kblk = (int)blockIdx.y;  // small key blocks see the most queries: first
+  const int b = bh / H, h = bh - b * H;
+  const int C = H * HS;
+  const size_t head = (size_t)bh * T * HS;
+  const bf16_t* Qh = Qg + head;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hi = lane >> 5;
+  const int kb0 = kblk * 128;
+  const int kw0 = kb0 + wid * 32;
+  const int mykey = kw0 + (lane & 31);
+
+  bf16x8 kf[HS / 16], vf[HS / 16];
+#pragma unroll
+  for (int kk = 0; kk < HS / 16; ++kk) {
+    if (mykey < T) {
+      kf[kk] = *reinterpret_cast<const bf16x8*>(Kg + head + (size_t)mykey * HS + 16 * kk + 8 * hi);
+      vf[kk] = *reinterpret_cast<const bf16x8*>(Vg + head + (size_t)mykey * HS + 16 * kk + 8 * hi);
+    } else {
+      kf[kk] = bf16x8{};
+      vf[kk] = bf16x8{};
+    }
+  }
+  floatx16 dk[HS / 32], dv[HS / 32];
+#pragma unroll
+  for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[dt][r] = 0.f;
+      dv[dt][r] = 0.f;
+    }
+
+  int qoff[HS / 16];
+#pragma unroll
+  for (int kk = 0; kk < HS / 16; ++kk) {
+    const int row = lane & 31;
+    qoff[kk] = row * RB + (((2 * kk + hi) ^ kv_swz<HS>(row)) << 4);
+  }
+  const int G = lane >> 4, s16 = lane & 15;
+  const int r0 = 4 * (G >> 1) + (s16 >> 2);
+  int toff[HS / 32];
+#pragma unroll
+  for (int dt = 0; dt < HS / 32; ++dt) {
+    const int d = dt * 32 + 16 * (G & 1) + 4 * (s16 & 3);
+    toff[dt] = r0 * RB + (((d >> 3) ^ kv_swz<HS>(r0)) << 4) + ((d >> 2) & 1) * 8;
+  }
+
+  const int nqt = (T - kb0 + BQ - 1) / BQ;  // query tiles i0 = kb0, kb0 + 64, ...
+  const float* Lrow = Lpad + (size_t)bh * Tpad;
+  const float* Drow = Dpad + (size_t)bh * Tpad;
+
+  auto issue = [&](char* dst, int i0) {
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const int inst = wid * LPW + q;
+      const int row = inst * RPI + lane / CPR;
+      const int chunk = (lane % CPR) ^ kv_swz<HS>(row);
+      const int qr = i0 + row;
+      const bool ok = qr < T;
+      const bf16_t* gq = ok ? Qh + (size_t)qr * HS + chunk * 8
+                            : reinterpret_cast<const bf16_t*>(&g_zero16);
+      const bf16_t* go = ok ? dOg + ((size_t)b * T + qr) * C + h * HS + chunk * 8
+                            : reinterpret_cast<const bf16_t*>(&g_zero16);
+      char* base = dst + inst * 1024;
+      __builtin_amdgcn_load_to_lds((void*)gq, GA_LDS(base), 16, 0, 0);
+      __builtin_amdgcn_load_to_lds((void*)go, GA_LDS(base + TILE), 16, 0, 0);
+    }
+    // L and D of the 64 queries (rows padded to Tpad, so always in bounds):
+    // lanes 0..15 of wave 0 fetch L, lanes 16..31 D, 16 bytes each
+    if (wid == 0 && lane < 32) {
+      const float* src = lane < 16 ? Lrow + i0 + 4 * lane : Drow + i0 + 4 * (lane - 16);
+      __builtin_amdgcn_load_to_lds((void*)src, GA_LDS(dst + 2 * TILE), 16, 0, 0);
+    }
+  };
+  issue(smem, kb0);
+
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) const bf16x8 lds_b128;
+  typedef float f4v __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) const f4v lds_f4;
+
+  auto tile = [&](auto mask_tag, const char* __restrict__ rd, char* __restrict__ wr, int in,
+                  int i0) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if (in >= 0) issue(wr, in);
+    const lds_char* lbase = (const lds_char*)rd;
+    floatx16 s[2], dp[2];
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s[qh][r] = 0.f;
+        dp[qh][r] = 0.f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < HS / 16; ++kk) {
+        const bf16x8 qa = *(lds_b128*)(lbase + qoff[kk] + qh * 32 * RB);
+        const bf16x8 ga = *(lds_b128*)(lbase + TILE + qoff[kk] + qh * 32 * RB);
+        s[qh] = mfma32(qa, kf[kk], s[qh]);
+        dp[qh] = mfma32(ga, vf[kk], dp[qh]);
+      }
+    }
+    // lane = key mykey; register r of qh <-> query i0 + qh*32 + 8(r/4) + 4hi + r%4
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int ql = qh * 32 + 8 * g + 4 * hi;
+        const f4v Lv = *(lds_f4*)(lbase + 2 * TILE + ql * 4);
+        const f4v Dv = *(lds_f4*)(lbase + 2 * TILE + 256 + ql * 4);
+        const float Ls[4] = {Lv[0], Lv[1], Lv[2], Lv[3]}, Ds[4] = {Dv[0], Dv[1], Dv[2], Dv[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const int q = i0 + ql + e;
+          float p = __builtin_amdgcn_exp2f(fmaf(s[qh][r], scale_log2, -Ls[e]));
+          float dpv = dp[qh][r];
+          if constexpr (DROP) {
+            const uint4 w = philox4x32_10(
+                make_uint4((uint32_t)mykey >> 2, (uint32_t)q, (uint32_t)bh, 1u), drop.k0, drop.k1);
+            const uint32_t k = mykey & 3;
+            const uint32_t wd = k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
+            const float z = wd >= drop.thresh ? drop.scale : 0.f;
+            s[qh][r] = p * z;
+            dp[qh][r] = p * (dpv * z - Ds[e]);
+          } else {
+            s[qh][r] = p;
+            dp[qh][r] = p * (dpv - Ds[e]);
+          }
+          const bool dead = q >= T || (MASK && mykey > q);
+          if (dead) {
+            s[qh][r] = 0.f;
+            dp[qh][r] = 0.f;
+          }
+        }
+      }
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS; transposing reads in the query order
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 pf, sf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pf[e] = (__bf16)s[qh][8 * u + e];
+          sf[e] = (__bf16)dp[qh][8 * u + e];
+        }
+        const int qb = qh * 32 + 16 * u;
+#pragma unroll
+        for (int dt = 0; dt < HS / 32; ++dt) {
+          v4i16 ro[2], rq[2];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            ro[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(lbase + TILE + toff[dt] +
+                                                           (qb + 8 * t) * RB));
+            rq[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)(lbase + toff[dt] + (qb + 8 * t) * RB));
+          }
+          typedef short v8i16 __attribute__((ext_vector_type(8)));
+          const v8i16 ov = {ro[0][0], ro[0][1], ro[0][2], ro[0][3],
+                            ro[1][0], ro[1][1], ro[1][2], ro[1][3]};
+          const v8i16 qv = {rq[0][0], rq[0][1], rq[0][2], rq[0][3],
+                            rq[1][0], rq[1][1], rq[1][2], rq[1][3]};
+          dv[dt] = mfma32(__builtin_bit_cast(bf16x8, ov), pf, dv[dt]);
+          dk[dt] = mfma32(__builtin_bit_cast(bf16x8, qv), sf, dk[dt]);
+        }
+      }
+  };
+
+  // the first two query tiles reach the block's keys' diagonal; a wave skips
+  // a tile wholly before its keys
+  const int n_mask = min(nqt, 2);
+  int it = 0;
+  for (; it < n_mask; ++it) {
+    wait_vmcnt<0>();
+    bar_nofence();
+    const int i0 = kb0 + it * BQ;
+    const int in = it + 1 < nqt ? i0 + BQ : -1;
+    char* wr = smem + ((it + 1) & 1) * STAGE;
+    if (i0 + BQ - 1 >= kw0)
+      tile(std::integral_constant<bool, true>{}, smem + (it & 1) * STAGE, wr, in, i0);
+    else if (in >= 0)
+      issue(wr, in);
+  }
+  for (; it < nqt; ++it) {
+    wait_vmcnt<0>();
+    bar_nofence();
+    const int i0 = kb0 + it * BQ;
+    const int in = it + 1 < nqt ? i0 + BQ : -1;
+    tile(std::integral_constant<bool, false>{}, smem + (it & 1) * STAGE,
+         smem + ((it + 1) & 1) * STAGE, in, i0);
+  }
+
+  if (mykey < T) {
+    bf16_t* row = dqkv + ((size_t)b * T + mykey) * 3 * C + (size_t)h * HS;
+#pragma unroll
+    for (int dt = 0; dt < HS / 32; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * hi;
+        uint2 wk, wv;
+        wk.x = pack_bf16x2(dk[dt][4 * g] * scale, dk[dt][4 * g + 1] * scale);
+        wk.y = pack_bf16x2(dk[dt][4 * g + 2] * scale, dk[dt][4 * g + 3] * scale);
+        wv.x = pack_bf16x2(dv[dt][4 * g], dv[dt][4 * g + 1]);
+        wv.y = pack_bf16x2(dv[dt][4 * g + 2], dv[dt][4 * g + 3]);
+        *reinterpret_cast<uint2*>(row + C + d0) = wk;
+        *reinterpret_cast<uint2*>(row + 2 * C + d0) = wv;
+      }
+  }
+}
+
+}  // namespace gpt_attn

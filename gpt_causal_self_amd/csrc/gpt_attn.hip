@@ -9,6 +9,7 @@
 #include <algorithm>
 
 #include "attn_bwd.cuh"
+#include "attn_bwd2.cuh"
 #include "handle.cuh"
 #include "layer_fwd.cuh"
 
@@ -76,6 +77,7 @@ int gpt_attn_create(gpt_attn_t* out, int C, int n_head, int max_B, int max_T, in
   h->part = (float*)(h->ws + L.part);
   h->part_elems = L.part_elems;
   h->ln = h->ws + L.ln;
+  h->rowstats = (float*)(h->ws + L.rowstats);
 
   *out = h;
   return GPT_ATTN_OK;
@@ -292,40 +294,44 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     }
     mark(h, 5, st);
     // ---- attention core
-    const dim3 dgrid((unsigned)((M * (long)H + 255) / 256));
-    const dim3 kgrid(B * H, (T + kBwdBK - 1) / kBwdBK);
-    const dim3 qgrid(B * H, (T + 127) / 128);
     const bf16_t* q = qkv;
     const bf16_t* k = qkv + head_elems;
     const bf16_t* v = qkv + 2 * head_elems;
     const dim3 vgrid((unsigned)(((long)M * (C / 8) + 255) / 256));
+    const int Tpad = (T + 63) / 64 * 64;
+    float* Dpad = h->rowstats;
+    float* Lpad = h->rowstats + (size_t)B * H * Tpad;
+    const dim3 kgrid2(B * H, (T + 127) / 128);
+    const dim3 qgrid2(B * H, (T + 127) / 128);
     if (hs == 64) {
-      hipLaunchKernelGGL(attn_delta_bf16_kernel<64>, vgrid, dim3(256), 0, st, dym, o, h->delta,
-                         B, H, T);
+      hipLaunchKernelGGL(attn_bwd_rowstats_kernel<64>, vgrid, dim3(256), 0, st, dym, o, h->lse,
+                         Dpad, Lpad, B, H, T, Tpad);
       if (drop) {
-        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<64, true>), kgrid, dim3(256), 0, st, q, k,
-                           v, dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
-        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<64, true>), qgrid, dim3(256), 0, st, q, k, v,
-                           dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
+        hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<64, true>), kgrid2, dim3(256), 0, st, q,
+                           k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
+        hipLaunchKernelGGL((attn_bwd_dq2_bf16_kernel<64, true>), qgrid2, dim3(256), 0, st, q, k,
+                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
       } else {
-        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<64>), kgrid, dim3(256), 0, st, q, k, v,
-                           dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, DropParams{});
-        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<64>), qgrid, dim3(256), 0, st, q, k, v, dym,
-                           h->lse, h->delta, dqkv, H, T, scale, scale_log2, DropParams{});
+        hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<64, false>), kgrid2, dim3(256), 0, st, q,
+                           k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2,
+                           DropParams{});
+        hipLaunchKernelGGL((attn_bwd_dq2_bf16_kernel<64, false>), qgrid2, dim3(256), 0, st, q, k,
+                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, DropParams{});
       }
     } else {
-      hipLaunchKernelGGL(attn_delta_bf16_kernel<32>, vgrid, dim3(256), 0, st, dym, o, h->delta,
-                         B, H, T);
+      hipLaunchKernelGGL(attn_bwd_rowstats_kernel<32>, vgrid, dim3(256), 0, st, dym, o, h->lse,
+                         Dpad, Lpad, B, H, T, Tpad);
       if (drop) {
-        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<32, true>), kgrid, dim3(256), 0, st, q, k,
-                           v, dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
-        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<32, true>), qgrid, dim3(256), 0, st, q, k, v,
-                           dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, dp);
+        hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<32, true>), kgrid2, dim3(256), 0, st, q,
+                           k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
+        hipLaunchKernelGGL((attn_bwd_dq2_bf16_kernel<32, true>), qgrid2, dim3(256), 0, st, q, k,
+                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
       } else {
-        hipLaunchKernelGGL((attn_bwd_dkdv_bf16_kernel<32>), kgrid, dim3(256), 0, st, q, k, v,
-                           dym, h->lse, h->delta, dqkv, H, T, scale, scale_log2, DropParams{});
-        hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<32>), qgrid, dim3(256), 0, st, q, k, v, dym,
-                           h->lse, h->delta, dqkv, H, T, scale, scale_log2, DropParams{});
+        hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<32, false>), kgrid2, dim3(256), 0, st, q,
+                           k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2,
+                           DropParams{});
+        hipLaunchKernelGGL((attn_bwd_dq2_bf16_kernel<32, false>), qgrid2, dim3(256), 0, st, q, k,
+                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, DropParams{});
       }
     }
     mark(h, 6, st);

@@ -52,6 +52,8 @@ struct gpt_attn_handle {
   float* delta;  // [B][H][T]     backward: rowsum(dO * O)
   float* part;   // split-K partial sums of weight gradients (fp32)
   void* ln;      // [B][T][C]     Pre-LN block: ln_1 of the input
+  float* rowstats;  // backward: L (log2 units) and D per softmax row, rows of
+                    // T rounded up to 64: [2][B][H][Tpad]
   size_t part_elems;
   // state of the last forward
   int saved, saved_B, saved_T;
@@ -90,7 +92,7 @@ int check_dims(int C, int n_head, int max_B, int max_T, int dtype) {
 }
 
 struct Layout {
-  size_t qkv, o, lse, dym, dqkv, delta, part, ln, total, part_elems;
+  size_t qkv, o, lse, dym, dqkv, delta, part, ln, rowstats, total, part_elems;
 };
 
 Layout layout(int C, int H, int max_B, int max_T, size_t es) {
@@ -106,6 +108,8 @@ Layout layout(int C, int H, int max_B, int max_T, size_t es) {
   L.part_elems = (size_t)kWgradSplits * C * 3 * C + (size_t)kColsumSplits * 3 * C;
   L.part = off;  off = align_up(off + L.part_elems * sizeof(float));
   L.ln = off;    off = align_up(off + BT * C * es);
+  L.rowstats = off;
+  off = align_up(off + 2 * (size_t)max_B * H * ((max_T + 63) / 64 * 64) * sizeof(float));
   L.total = off;
   return L;
 }
