@@ -405,6 +405,36 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
         const f4v Lv = *(lds_f4*)(lbase + 2 * TILE + ql * 4);
         const f4v Dv = *(lds_f4*)(lbase + 2 * TILE + 256 + ql * 4);
         const float Ls[4] = {Lv[0], Lv[1], Lv[2], Lv[3]}, Ds[4] = {Dv[0], Dv[1], Dv[2], Dv[3]};
+        uint32_t keepw[4] = {0u, 0u, 0u, 0u};
+        if constexpr (DROP) {
+          // The 4 lanes of a quad hold keys 4a..4a+3 (same counter word a)
+          // and need, for each of the 4 queries of this register group, their
+          // own word of that query's Philox block: lane t computes the block
+          // of query ql + t, then a 4 x 4 transpose inside the quad (select
+          // word t ^ r, move it across lane distance r) hands every lane its
+          // word of every block.
+          const int t = lane & 3;
+          const uint4 w = philox4x32_10(
+              make_uint4((uint32_t)mykey >> 2, (uint32_t)(i0 + ql + t), (uint32_t)bh, 1u), drop.k0,
+              drop.k1);
+          const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+          uint32_t got[4];  // got[r]: word for this key of query ql + (t ^ r)
+          got[0] = wv[t];
+#pragma unroll
+          for (int r = 1; r < 4; ++r) {
+            const int si = t ^ r;
+            const uint32_t x = si == 0 ? wv[0] : si == 1 ? wv[1] : si == 2 ? wv[2] : wv[3];
+            // quad_perm xor 1, 2, 3: [1,0,3,2], [2,3,0,1], [3,2,1,0]
+            got[r] = (uint32_t)(r == 1   ? __builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false)
+                                : r == 2 ? __builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false)
+                                         : __builtin_amdgcn_update_dpp(0, (int)x, 0x1B, 0xF, 0xF, false));
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = e ^ t;
+            keepw[e] = r == 0 ? got[0] : r == 1 ? got[1] : r == 2 ? got[2] : got[3];
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
@@ -412,11 +442,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
           float p = __builtin_amdgcn_exp2f(fmaf(s[qh][r], scale_log2, -Ls[e]));
           float dpv = dp[qh][r];
           if constexpr (DROP) {
-            const uint4 w = philox4x32_10(
-                make_uint4((uint32_t)mykey >> 2, (uint32_t)q, (uint32_t)bh, 1u), drop.k0, drop.k1);
-            const uint32_t k = mykey & 3;
-            const uint32_t wd = k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w;
-            const float z = wd >= drop.thresh ? drop.scale : 0.f;
+            const float z = keepw[e] >= drop.thresh ? drop.scale : 0.f;
             s[qh][r] = p * z;
             dp[qh][r] = p * (dpv * z - Ds[e]);
           } else {
