@@ -167,7 +167,7 @@ struct Epi2RowMajor {
   }
   // staged path: bias is added before rounding into the LDS tile
   static constexpr bool kStaged = true;
-  __device__ __forceinline__ float bias_at(int n) const { return bias ? bf2f(bias[n]) : 0.f; }
+  __device__ __forceinline__ const bf16_t* bias_ptr() const { return bias; }
   __device__ __forceinline__ void store8(int m, int n, uint4 w) const {
     *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = w;
   }
@@ -205,7 +205,7 @@ struct Epi2QKV {
     *reinterpret_cast<uint2*>(qkv + off) = w;
   }
   static constexpr bool kStaged = true;
-  __device__ __forceinline__ float bias_at(int n) const { return bias ? bf2f(bias[n]) : 0.f; }
+  __device__ __forceinline__ const bf16_t* bias_ptr() const { return bias; }
   __device__ __forceinline__ void store8(int m, int n, uint4 w) const {
     *reinterpret_cast<uint4*>(qkv + row_off(m) + col_off(n)) = w;
   }
@@ -236,7 +236,7 @@ struct Epi2Gelu {
     *reinterpret_cast<uint2*>(out + (size_t)m * ldc + n) = w;
   }
   static constexpr bool kStaged = true;
-  __device__ __forceinline__ float bias_at(int n) const { return bias ? bf2f(bias[n]) : 0.f; }
+  __device__ __forceinline__ const bf16_t* bias_ptr() const { return bias; }
   __device__ __forceinline__ void store8(int m, int n, uint4 w) const {
     *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = w;
   }
@@ -322,8 +322,14 @@ void gemm2_kernel(
   // that still fits the CU's 160 KB.
   constexpr int kEpiBytes = Staged<Epi>::value ? BM * (BN + 8) * 2 : 0;
   constexpr int kSmemAll =
-      kEpiBytes > Cfg::kSmem && kEpiBytes <= 160 * 1024 ? kEpiBytes : Cfg::kSmem;
-  __shared__ __align__(1024) char smem[kSmemAll];
+      kEpiBytes > Cfg::kSmem && kEpiBytes + BN * 2 <= 160 * 1024 ? kEpiBytes : Cfg::kSmem;
+  constexpr bool kStagedEpi = Staged<Epi>::value && BM * (BN + 8) * 2 <= kSmemAll;
+  // The staged epilogue reads the tile's bias columns from LDS, placed after
+  // the ring / staging area.
+  constexpr int kBiasOff = (kSmemAll + 15) / 16 * 16;
+  constexpr int kLdsBytes = kStagedEpi ? kBiasOff + BN * 2 : kSmemAll;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS");
+  __shared__ __align__(1024) char smem[kLdsBytes];
 
   const int tiles_n = (N + BN - 1) / BN;
   const int tile = xcd_swizzle(blockIdx.x, gridDim.x);
@@ -349,6 +355,21 @@ void gemm2_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  if constexpr (kStagedEpi) {
+    // Bias columns n0 .. n0+BN-1 go straight to LDS (one 16-byte chunk per
+    // lane of wave 0; chunks past N or a NULL bias read zeros).  Issued
+    // before the ring, this load is older than every ring load of wave 0,
+    // so the ring's vmcnt waits cover it; the barrier after the main loop
+    // publishes it.
+    static_assert(BN % 8 == 0 && BN / 8 <= 64, "bias tile");
+    if (wid == 0 && lane < BN / 8) {
+      const bf16_t* bp = epi.bias_ptr();
+      const int n = n0 + 8 * lane;
+      const bf16_t* g = (bp && n < N) ? bp + n : reinterpret_cast<const bf16_t*>(&g_zero16);
+      __builtin_amdgcn_load_to_lds((void*)g, GA_LDS(smem + kBiasOff), 16, 0, 0);
+    }
+  }
+
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < nk) {
@@ -371,7 +392,7 @@ void gemm2_kernel(
         Bm, ldb, m0, n0, M, N, kbeg + kn * BK, kend, wid, lane, wm, wn, acc);
   }
 
-  if constexpr (Staged<Epi>::value && BM * (BN + 8) * 2 <= kSmemAll) {
+  if constexpr (kStagedEpi) {
     // ---- staged epilogue: bias + bf16 rounding into an LDS tile [BM][BN+8],
     // then every 8 lanes store one 128-byte run of a row.
     constexpr int SP = BN + 8;  // pitch (elements); 16-byte aligned rows
@@ -382,10 +403,9 @@ void gemm2_kernel(
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int cl = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);  // local column
-        const int n = n0 + cl;
-        float b[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = (n + e < N) ? epi.bias_at(n + e) : 0.f;
+        const uint2 bu = *reinterpret_cast<const uint2*>(smem + kBiasOff + cl * 2);
+        const float b[4] = {bf2f(bu.x & 0xffff), bf2f(bu.x >> 16), bf2f(bu.y & 0xffff),
+                            bf2f(bu.y >> 16)};
 #pragma unroll
         for (int i = 0; i < MT; ++i) {
           const int rl = wm * WTM + i * 32 + (lane & 31);
