@@ -131,6 +131,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
   }
   const int G = lane >> 4, s16 = lane & 15;
   const int r0 = 4 * (G >> 1) + (s16 >> 2);
+  // t = 1 (rows r0 + 8) flips chunk bit 1 of the swizzle: offset bit 5.
   int toff[HS / 32];
 #pragma unroll
   for (int dt = 0; dt < HS / 32; ++dt) {
@@ -225,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
 #pragma unroll
           for (int t = 0; t < 2; ++t)
             rv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(lbase + toff[dt] + (kb + 8 * t) * RB));
+                (__attribute__((address_space(3))) v4i16*)(lbase + tr_off<RB>(toff[dt], t) + kb * RB));
           typedef short v8i16 __attribute__((ext_vector_type(8)));
           const v8i16 kv = {rv[0][0], rv[0][1], rv[0][2], rv[0][3],
                             rv[1][0], rv[1][1], rv[1][2], rv[1][3]};
@@ -334,6 +335,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
   }
   const int G = lane >> 4, s16 = lane & 15;
   const int r0 = 4 * (G >> 1) + (s16 >> 2);
+  // t = 1 (rows r0 + 8) flips chunk bit 1 of the swizzle: offset bit 5.
   int toff[HS / 32];
 #pragma unroll
   for (int dt = 0; dt < HS / 32; ++dt) {
@@ -475,10 +477,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             ro[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(lbase + TILE + toff[dt] +
-                                                           (qb + 8 * t) * RB));
+                (__attribute__((address_space(3))) v4i16*)(lbase + TILE + tr_off<RB>(toff[dt], t) +
+                                                           qb * RB));
             rq[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(lbase + toff[dt] + (qb + 8 * t) * RB));
+                (__attribute__((address_space(3))) v4i16*)(lbase + tr_off<RB>(toff[dt], t) + qb * RB));
           }
           typedef short v8i16 __attribute__((ext_vector_type(8)));
           const v8i16 ov = {ro[0][0], ro[0][1], ro[0][2], ro[0][3],

@@ -50,9 +50,28 @@ constexpr int kAttnBK = 64;   // keys per tile
 //    rescaling: the running reference max only moves (rescaling l and the
 //    accumulators) when a tile's max exceeds it by more than 8 in log2 units,
 //    so probabilities stay <= 2^8 and most tiles skip the rescale.
+// Chunk swizzle of a key row.  LDS has 64 four-byte banks (256 bytes per
+// bank line), so a 128-byte row (HS = 64) shares its bank line with one
+// neighbour and a 64-byte row (HS = 32) with three.  The swizzle keeps both
+// read patterns conflict-free:
+//  * b128 fragment reads: 16 lanes read one chunk of 16 consecutive rows;
+//    rows of the same bank-line position must use distinct chunks, so the
+//    swizzle runs over bits 1..3 (HS = 64) or 2..3 (HS = 32) of the row;
+//  * transposing reads: 32 lanes read chunks 0..3 (or 4..7) of 4
+//    consecutive rows 4a..4a+3; for HS = 64 rows 4a and 4a+2 must land in
+//    different chunk halves, so bit 1 of the row moves the chunk by 4.
+// The swizzle depends on bits 1..3 of the row only: it repeats every 16 rows.
 template <int HS>
 __device__ __forceinline__ int kv_swz(int row) {
-  return HS == 64 ? (row & 7) : ((row >> 1) & 3);
+  return HS == 64 ? ((((row >> 1) & 1) << 2) | ((row >> 2) & 3)) : ((row >> 2) & 3);
+}
+
+// Offset of a transposing read 8t rows below the one at offset `off`
+// (t = 0, 1): for both head sizes kv_swz(r + 8) = kv_swz(r) ^ 2, i.e. chunk
+// bit 1 (offset bit 5) flips; rows are RB bytes apart.
+template <int RB>
+__device__ __forceinline__ int tr_off(int off, int t) {
+  return t ? ((off ^ 32) + 8 * RB) : off;
 }
 
 // DROP: dropout on the attention weights (philox.cuh): the row sum uses
@@ -102,10 +121,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
   float m = -INFINITY, l = 0.f;
 
   // Loop-invariant LDS offsets.  K fragment (row kt*32 + lane%32, chunk
-  // 2kk + hi): the row's swizzle is (lane & 7) for every kt (rows differ by
-  // multiples of 8), so only kk and the lane matter.  V transposing reads
-  // (row kb + 8t + 4(G/2) + s/4, column dt*32 + 16(G%2) + 4(s%4)): kb + 8t is
-  // a multiple of 8, so the swizzle depends on the lane part r0 only.
+  // 2kk + hi): rows differ from lane%32 by multiples of 32, which leave the
+  // swizzle unchanged, so only kk and the lane matter.  V transposing reads
+  // (row kb + 8t + 4(G/2) + s/4, column dt*32 + 16(G%2) + 4(s%4)): kb is a
+  // multiple of 16, so the swizzle depends on t and the lane part r0 only.
   int koff[HS / 16];
 #pragma unroll
   for (int kk = 0; kk < HS / 16; ++kk) {
@@ -114,12 +133,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
   }
   const int G = lane >> 4, s16 = lane & 15;
   const int r0 = 4 * (G >> 1) + (s16 >> 2);
-  int voff[HS / 32];
+  int voff[2][HS / 32];
 #pragma unroll
-  for (int dt = 0; dt < HS / 32; ++dt) {
-    const int d = dt * 32 + 16 * (G & 1) + 4 * (s16 & 3);
-    voff[dt] = r0 * RB + (((d >> 3) ^ kv_swz<HS>(r0)) << 4) + ((d >> 2) & 1) * 8;
-  }
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int dt = 0; dt < HS / 32; ++dt) {
+      const int d = dt * 32 + 16 * (G & 1) + 4 * (s16 & 3);
+      const int r = r0 + 8 * t;
+      voff[t][dt] = r * RB + (((d >> 3) ^ kv_swz<HS>(r)) << 4) + ((d >> 2) & 1) * 8;
+    }
 
   const int kv_end = min(T, (qt + 1) * kAttnBQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
@@ -238,9 +260,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     }
     // ---- O^T += V^T P^T; V^T operand by transposing reads in the key order
     // of the P registers: element e <-> key kb + 8(e/4) + 4*hi + e%4.
-    int va[HS / 32];
+    int va[2][HS / 32];
 #pragma unroll
-    for (int dt = 0; dt < HS / 32; ++dt) va[dt] = TILE + voff[dt];
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int dt = 0; dt < HS / 32; ++dt) va[t][dt] = TILE + voff[t][dt];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -255,7 +279,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
 #pragma unroll
           for (int t = 0; t < 2; ++t)
             rv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(lbase + va[dt] + (kb + 8 * t) * RB));
+                (__attribute__((address_space(3))) v4i16*)(lbase + va[t][dt] + kb * RB));
           typedef short v8i16 __attribute__((ext_vector_type(8)));
           const v8i16 vv = {rv[0][0], rv[0][1], rv[0][2], rv[0][3],
                             rv[1][0], rv[1][1], rv[1][2], rv[1][3]};

@@ -13,7 +13,7 @@
 //
 // LDS layouts (16-byte chunks, XOR-swizzled so MFMA operand reads spread over
 // the banks):
-//   k-contiguous operand: [row][BK], chunk c of row r at slot c ^ (r & 7);
+//   k-contiguous operand: [row][BK], chunk c of row r at slot c ^ kc_swz(r);
 //     an MFMA fragment (32 rows x 16 k) is one ds_read_b128 per lane.
 //   row-contiguous operand: [BK][ROWS], chunk c of k-row r at slot
 //     c ^ 4*(r & 3); a fragment is two ds_read_b64_tr_b16 per lane.  Within a
@@ -77,11 +77,14 @@ struct Gemm2Cfg {
 // Issue the global->LDS loads of one operand tile (ROWS x BK) for this wave.
 // KC: source (row, k) at src[row*ld + k]; RC: at src[k*ld + row].
 // Slot swizzle of a k-contiguous tile: chunk c of row r lives at c ^ kc_swz(r).
-// BK = 64 (8 chunks a row): r & 7.  BK = 32 (4 chunks): (r >> 1) & 3, so the
-// 64-byte rows of 8 consecutive rows cover distinct bank groups.
+// LDS has 64 four-byte banks (256-byte bank lines); a fragment read serves
+// 16 lanes = 16 consecutive rows at one chunk per pass.  BK = 64 (128-byte
+// rows, two per bank line): rows of equal parity need distinct slots, so
+// the swizzle is (r >> 1) & 7.  BK = 32 (64-byte rows, four per line):
+// (r >> 2) & 3.
 template <int BK>
 __device__ __forceinline__ int kc_swz(int row) {
-  return BK == 64 ? (row & 7) : ((row >> 1) & 3);
+  return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
 template <int ROWS, int BK, bool KC>
