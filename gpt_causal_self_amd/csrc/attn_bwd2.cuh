@@ -142,19 +142,25 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
   const int kv_end = min(T, (qt + 1) * 128);
   const int nkv = (kv_end + BKV - 1) / BKV;
 
+  // Loop-invariant per-lane source offsets within a tile; only a tile that
+  // crosses T checks rows (rows past T read a zero chunk).
+  int src_off[LPW];
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    const int row = (wid * LPW + q) * RPI + lane / CPR;
+    src_off[q] = row * HS + ((lane % CPR) ^ kv_swz<HS>(row)) * 8;
+  }
   auto issue = [&](char* dst, int j0) {
+    const bf16_t* kt0 = Kh + (size_t)j0 * HS;
+    const bf16_t* vt0 = Vh + (size_t)j0 * HS;
+    const bool full = j0 + BKV <= T;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
-      const int inst = wid * LPW + q;
-      const int row = inst * RPI + lane / CPR;
-      const int chunk = (lane % CPR) ^ kv_swz<HS>(row);
-      const int key = j0 + row;
-      const bool ok = key < T;
-      const bf16_t* gk = ok ? Kh + (size_t)key * HS + chunk * 8
-                            : reinterpret_cast<const bf16_t*>(&g_zero16);
-      const bf16_t* gv = ok ? Vh + (size_t)key * HS + chunk * 8
-                            : reinterpret_cast<const bf16_t*>(&g_zero16);
-      char* base = dst + inst * 1024;
+      const int row = (wid * LPW + q) * RPI + lane / CPR;
+      const bool ok = full || j0 + row < T;
+      const bf16_t* gk = ok ? kt0 + src_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
+      const bf16_t* gv = ok ? vt0 + src_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
+      char* base = dst + (wid * LPW + q) * 1024;
       __builtin_amdgcn_load_to_lds((void*)gk, GA_LDS(base), 16, 0, 0);
       __builtin_amdgcn_load_to_lds((void*)gv, GA_LDS(base + TILE), 16, 0, 0);
     }
@@ -347,18 +353,28 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
   const float* Lrow = Lpad + (size_t)bh * Tpad;
   const float* Drow = Dpad + (size_t)bh * Tpad;
 
+  // Loop-invariant per-lane (row, chunk) of each load; a query tile at i0
+  // adds i0 rows.  Only a tile that crosses T checks rows.
+  int q_off[LPW], o_off[LPW];
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    const int row = (wid * LPW + q) * RPI + lane / CPR;
+    const int c8 = ((lane % CPR) ^ kv_swz<HS>(row)) * 8;
+    q_off[q] = row * HS + c8;
+    o_off[q] = row * C + c8;
+  }
+  const bf16_t* dOh = dOg + (size_t)b * T * C + h * HS;
   auto issue = [&](char* dst, int i0) {
+    const bf16_t* qt0 = Qh + (size_t)i0 * HS;
+    const bf16_t* ot0 = dOh + (size_t)i0 * C;
+    const bool full = i0 + BQ <= T;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
       const int inst = wid * LPW + q;
       const int row = inst * RPI + lane / CPR;
-      const int chunk = (lane % CPR) ^ kv_swz<HS>(row);
-      const int qr = i0 + row;
-      const bool ok = qr < T;
-      const bf16_t* gq = ok ? Qh + (size_t)qr * HS + chunk * 8
-                            : reinterpret_cast<const bf16_t*>(&g_zero16);
-      const bf16_t* go = ok ? dOg + ((size_t)b * T + qr) * C + h * HS + chunk * 8
-                            : reinterpret_cast<const bf16_t*>(&g_zero16);
+      const bool ok = full || i0 + row < T;
+      const bf16_t* gq = ok ? qt0 + q_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
+      const bf16_t* go = ok ? ot0 + o_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
       char* base = dst + inst * 1024;
       __builtin_amdgcn_load_to_lds((void*)gq, GA_LDS(base), 16, 0, 0);
       __builtin_amdgcn_load_to_lds((void*)go, GA_LDS(base + TILE), 16, 0, 0);

@@ -147,21 +147,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
   const int nkv = (kv_end + BKV - 1) / BKV;
 
   // Loads of the K and V tile starting at key j0 into the ring stage at dst.
-  auto issue = [&](char* dst, int j0) {
+  // Per-lane source offsets within a tile are loop-invariant: lane -> (row,
+  // chunk) of load q; a tile at key j0 adds j0 * HS.  Only a tile that
+  // crosses T needs the row check (rows past T read a zero chunk).
+  int src_off[LPW];
 #pragma unroll
-    for (int q = 0; q < LPW; ++q) {
-      const int inst = wid * LPW + q;
-      const int row = inst * RPI + lane / CPR;
-      const int chunk = (lane % CPR) ^ kv_swz<HS>(row);
-      const int key = j0 + row;
-      const bool ok = key < T;
-      const bf16_t* gk = ok ? Kh + (size_t)key * HS + chunk * 8
-                            : reinterpret_cast<const bf16_t*>(&g_zero16);
-      const bf16_t* gv = ok ? Vh + (size_t)key * HS + chunk * 8
-                            : reinterpret_cast<const bf16_t*>(&g_zero16);
-      char* base = dst + inst * 1024;
-      __builtin_amdgcn_load_to_lds((void*)gk, GA_LDS(base), 16, 0, 0);
-      __builtin_amdgcn_load_to_lds((void*)gv, GA_LDS(base + TILE), 16, 0, 0);
+  for (int q = 0; q < LPW; ++q) {
+    const int row = (wid * LPW + q) * RPI + lane / CPR;
+    src_off[q] = row * HS + ((lane % CPR) ^ kv_swz<HS>(row)) * 8;
+  }
+  auto issue = [&](char* dst, int j0) {
+    const bf16_t* kt0 = Kh + (size_t)j0 * HS;
+    const bf16_t* vt0 = Vh + (size_t)j0 * HS;
+    if (j0 + BKV <= T) {
+#pragma unroll
+      for (int q = 0; q < LPW; ++q) {
+        char* base = dst + (wid * LPW + q) * 1024;
+        __builtin_amdgcn_load_to_lds((void*)(kt0 + src_off[q]), GA_LDS(base), 16, 0, 0);
+        __builtin_amdgcn_load_to_lds((void*)(vt0 + src_off[q]), GA_LDS(base + TILE), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < LPW; ++q) {
+        const int row = (wid * LPW + q) * RPI + lane / CPR;
+        const bool ok = j0 + row < T;
+        const bf16_t* gk = ok ? kt0 + src_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
+        const bf16_t* gv = ok ? vt0 + src_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
+        char* base = dst + (wid * LPW + q) * 1024;
+        __builtin_amdgcn_load_to_lds((void*)gk, GA_LDS(base), 16, 0, 0);
+        __builtin_amdgcn_load_to_lds((void*)gv, GA_LDS(base + TILE), 16, 0, 0);
+      }
     }
   };
 
@@ -183,9 +198,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     if (jn >= 0) issue(wr, jn);
     const lds_char* lbase = (const lds_char*)rd;
     // ---- S^T = K Q^T for keys j0 .. j0+63
-    int ka[HS / 16];
-#pragma unroll
-    for (int kk = 0; kk < HS / 16; ++kk) ka[kk] = koff[kk];
     floatx16 sc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -193,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
       for (int r = 0; r < 16; ++r) sc[kt][r] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < HS / 16; ++kk) {
-        const bf16x8 kf = *(lds_b128*)(lbase + ka[kk] + kt * 32 * RB);
+        const bf16x8 kf = *(lds_b128*)(lbase + koff[kk] + kt * 32 * RB);
         sc[kt] = mfma32(kf, qf[kk], sc[kt]);
       }
     }
@@ -260,11 +272,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     }
     // ---- O^T += V^T P^T; V^T operand by transposing reads in the key order
     // of the P registers: element e <-> key kb + 8(e/4) + 4*hi + e%4.
-    int va[2][HS / 32];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int dt = 0; dt < HS / 32; ++dt) va[t][dt] = TILE + voff[t][dt];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
 #pragma unroll
           for (int t = 0; t < 2; ++t)
             rv[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4i16*)(lbase + va[t][dt] + kb * RB));
+                (__attribute__((address_space(3))) v4i16*)(lbase + TILE + voff[t][dt] + kb * RB));
           typedef short v8i16 __attribute__((ext_vector_type(8)));
           const v8i16 vv = {rv[0][0], rv[0][1], rv[0][2], rv[0][3],
                             rv[1][0], rv[1][1], rv[1][2], rv[1][3]};
