@@ -92,12 +92,49 @@ __device__ __forceinline__ void g2_issue_check() {
   static_assert(KC || ROWS >= 128, "row-contiguous operand tiles need >= 128 rows");
 }
 
+// Per-lane source offsets of one operand tile's loads (element offsets at
+// k0 = 0 relative to the tile's first row / column); loop-invariant, so a
+// k-tile adds only its k offset.
+template <int ROWS, int BK, bool KC, int NW = 4>
+struct G2Off {
+  static constexpr int kPerWave = ROWS * BK * 2 / 1024 / NW;
+  int off[kPerWave];
+  __device__ __forceinline__ void init(int ld, int wid, int lane) {
+#pragma unroll
+    for (int q = 0; q < kPerWave; ++q) {
+      const int inst = wid * kPerWave + q;
+      if (KC) {
+        constexpr int CPK = BK / 8;
+        const int row = inst * (64 / CPK) + lane / CPK;
+        off[q] = row * ld + ((lane % CPK) ^ kc_swz<BK>(row)) * 8;
+      } else {
+        constexpr int CPR = ROWS / 8;
+        constexpr int RPI = 64 / CPR;
+        const int krow = inst * RPI + lane / CPR;
+        off[q] = krow * ld + ((lane % CPR) ^ ((krow & 3) << 2)) * 8;
+      }
+    }
+  }
+};
+
+// Issue the global->LDS loads of one operand tile (ROWS x BK) for this wave.
+// KC: source (row, k) at src[row*ld + k]; RC: at src[k*ld + row].  A tile
+// wholly inside the matrix (rows and k) takes the precomputed offsets; a
+// ragged one checks every chunk and reads the zero block outside.
 template <int ROWS, int BK, bool KC, int NW = 4>
 __device__ __forceinline__ void g2_issue(const bf16_t* __restrict__ src, int ld, int row0,
                                          int nrows, int k0, int kend, char* lds, int wid,
-                                         int lane) {
+                                         int lane, const G2Off<ROWS, BK, KC, NW>& po) {
   constexpr int kPerWave = ROWS * BK * 2 / 1024 / NW;
   g2_issue_check<ROWS, BK, KC>();
+  if (row0 + ROWS <= nrows && k0 + BK <= kend) {
+    const bf16_t* base = KC ? src + (size_t)row0 * ld + k0 : src + (size_t)k0 * ld + row0;
+#pragma unroll
+    for (int q = 0; q < kPerWave; ++q)
+      __builtin_amdgcn_load_to_lds((void*)(base + po.off[q]),
+                                   GA_LDS(lds + (wid * kPerWave + q) * 1024), 16, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < kPerWave; ++q) {
     const int inst = wid * kPerWave + q;  // 1 KB block index within the tile
@@ -286,14 +323,16 @@ __device__ __forceinline__ void g2_step(const char* __restrict__ rd, char* __res
                                         const bf16_t* __restrict__ Bm, int ldb, int m0, int n0,
                                         int M, int N, int kload, int kend, int wid, int lane,
                                         int wm, int wn,
-                                        floatx16 (&acc)[BM / WGM / 32][BN / WGN / 32]) {
+                                        floatx16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                        const G2Off<BM, BK, A_KC, WGM * WGN>& pa,
+                                        const G2Off<BN, BK, B_KC, WGM * WGN>& pb) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MT = WTM / 32, NT = WTN / 32;
   constexpr int kA = BM * BK * 2;
   if (load) {
-    g2_issue<BM, BK, A_KC, NW>(A, lda, m0, M, kload, kend, wr, wid, lane);
-    g2_issue<BN, BK, B_KC, NW>(Bm, ldb, n0, N, kload, kend, wr + kA, wid, lane);
+    g2_issue<BM, BK, A_KC, NW>(A, lda, m0, M, kload, kend, wr, wid, lane, pa);
+    g2_issue<BN, BK, B_KC, NW>(Bm, ldb, n0, N, kload, kend, wr + kA, wid, lane, pb);
   }
 #pragma unroll
   for (int kk = 0; kk < BK / 16; ++kk) {
@@ -373,12 +412,17 @@ void gemm2_kernel(
     }
   }
 
+  G2Off<BM, BK, A_KC, NW> pa;
+  G2Off<BN, BK, B_KC, NW> pb;
+  pa.init(lda, wid, lane);
+  pb.init(ldb, wid, lane);
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
     if (s < nk) {
       char* sa = smem + s * Cfg::kStage;
-      g2_issue<BM, BK, A_KC, NW>(A, lda, m0, M, kbeg + s * BK, kend, sa, wid, lane);
-      g2_issue<BN, BK, B_KC, NW>(Bm, ldb, n0, N, kbeg + s * BK, kend, sa + Cfg::kA, wid, lane);
+      g2_issue<BM, BK, A_KC, NW>(A, lda, m0, M, kbeg + s * BK, kend, sa, wid, lane, pa);
+      g2_issue<BN, BK, B_KC, NW>(Bm, ldb, n0, N, kbeg + s * BK, kend, sa + Cfg::kA, wid, lane,
+                                 pb);
     }
 
   for (int kt = 0; kt < nk; ++kt) {
@@ -392,7 +436,7 @@ void gemm2_kernel(
     const int kn = kt + NSTAGE - 1;
     g2_step<BM, BN, BK, A_KC, B_KC, WGM, WGN>(
         smem + (kt % NSTAGE) * Cfg::kStage, smem + (kn % NSTAGE) * Cfg::kStage, kn < nk, A, lda,
-        Bm, ldb, m0, n0, M, N, kbeg + kn * BK, kend, wid, lane, wm, wn, acc);
+        Bm, ldb, m0, n0, M, N, kbeg + kn * BK, kend, wid, lane, wm, wn, acc, pa, pb);
   }
 
   if constexpr (kStagedEpi) {
