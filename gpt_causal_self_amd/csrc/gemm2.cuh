@@ -87,9 +87,12 @@ __device__ __forceinline__ int kc_swz(int row) {
   return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
+// A row-contiguous tile's k-rows hold ROWS/8 chunks; the swizzle XORs the
+// chunk index with 0, 4, 8 or 12, which maps [0, ROWS/8) onto itself when
+// ROWS/8 is a multiple of 16.
 template <int ROWS, int BK, bool KC>
 __device__ __forceinline__ void g2_issue_check() {
-  static_assert(KC || ROWS >= 128, "row-contiguous operand tiles need >= 128 rows");
+  static_assert(KC || (ROWS % 128 == 0), "row-contiguous operand tiles need 128 | ROWS");
 }
 
 // Per-lane source offsets of one operand tile's loads (element offsets at
@@ -109,9 +112,9 @@ struct G2Off {
         off[q] = row * ld + ((lane % CPK) ^ kc_swz<BK>(row)) * 8;
       } else {
         constexpr int CPR = ROWS / 8;
-        constexpr int RPI = 64 / CPR;
-        const int krow = inst * RPI + lane / CPR;
-        off[q] = krow * ld + ((lane % CPR) ^ ((krow & 3) << 2)) * 8;
+        const int idx = inst * 64 + lane;  // chunk index within the tile
+        const int krow = idx / CPR;
+        off[q] = krow * ld + ((idx % CPR) ^ ((krow & 3) << 2)) * 8;
       }
     }
   }
@@ -150,9 +153,9 @@ __device__ __forceinline__ void g2_issue(const bf16_t* __restrict__ src, int ld,
                                     : reinterpret_cast<const bf16_t*>(&g_zero16);
     } else {
       constexpr int CPR = ROWS / 8;               // chunks per k-row
-      constexpr int RPI = 64 / CPR;               // k-rows per instruction
-      const int krow = inst * RPI + lane / CPR;
-      const int slot = lane % CPR;
+      const int idx = inst * 64 + lane;           // chunk index within the tile
+      const int krow = idx / CPR;
+      const int slot = idx % CPR;
       const int chunk = slot ^ ((krow & 3) << 2);
       const int gk = k0 + krow, gr = row0 + chunk * 8;
       g = (gk < kend && gr < nrows) ? src + (size_t)gk * ld + gr

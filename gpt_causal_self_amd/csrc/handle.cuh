@@ -30,10 +30,10 @@
 // MLP: c_fc [C -> 4C] with the GELU epilogue, c_proj [4C -> C] (waves per
 // SIMD as the last value).
 #ifndef GA_FC_TILE
-#define GA_FC_TILE 256, 256, 2, 64, 2, 4, true, false, 1
+#define GA_FC_TILE 192, 384, 2, 64, 2, 4, true, false, 1
 #endif
 #ifndef GA_FCPROJ_TILE
-#define GA_FCPROJ_TILE 128, 128, 3, 32, 2, 2, true, false, 2
+#define GA_FCPROJ_TILE 128, 128, 3, 32, 2, 2, true, false, 3
 #endif
 
 
