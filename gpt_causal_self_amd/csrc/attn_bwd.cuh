@@ -264,4 +264,25 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __res
   }
 }
 
+// Column sums of S partial rows: out[c] = sum_k part[k * N + c].  One block
+// per 64 columns; its 4 waves split the partial rows (coalesced across the
+// 64 columns) and combine through LDS, so even N = 768 spreads over 12
+// blocks and no thread walks all S rows.
+template <class T_>
+__global__ __launch_bounds__(256) void reduce_colparts_kernel(const float* __restrict__ part,
+                                                              int S, int N,
+                                                              T_* __restrict__ out) {
+  __shared__ float red[4][64];
+  const int tid = threadIdx.x, c = tid & 63, sl = tid >> 6;
+  const int col = blockIdx.x * 64 + c;
+  float s = 0.f;
+  if (col < N) {
+#pragma unroll 4
+    for (int k = sl; k < S; k += 4) s += part[(size_t)k * N + col];
+  }
+  red[sl][c] = s;
+  __syncthreads();
+  if (sl == 0 && col < N) store1(out + col, (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]));
+}
+
 }  // namespace gpt_attn

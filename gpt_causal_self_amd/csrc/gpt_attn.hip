@@ -289,8 +289,8 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     if (db_proj) {
       hipLaunchKernelGGL(colsum_bf16_kernel, dim3((C + 63) / 64, bcs), dim3(256), 0, st,
                          (const bf16_t*)dY, M, C, C, brows, cpart);
-      hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3((C + 255) / 256), dim3(256), 0, st,
-                         cpart, bcs, (size_t)C, (size_t)C, (bf16_t*)db_proj);
+      hipLaunchKernelGGL(reduce_colparts_kernel<bf16_t>, dim3((C + 63) / 64), dim3(256), 0, st,
+                         cpart, bcs, C, (bf16_t*)db_proj);
     }
     mark(h, 5, st);
     // ---- attention core
@@ -348,8 +348,8 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     if (db_attn) {
       hipLaunchKernelGGL(colsum_bf16_kernel, dim3((N3 + 63) / 64, bcs), dim3(256), 0, st, dqkv, M,
                          N3, N3, brows, cpart);
-      hipLaunchKernelGGL(reduce_partials_kernel<bf16_t>, dim3((N3 + 255) / 256), dim3(256), 0,
-                         st, cpart, bcs, (size_t)N3, (size_t)N3, (bf16_t*)db_attn);
+      hipLaunchKernelGGL(reduce_colparts_kernel<bf16_t>, dim3((N3 + 63) / 64), dim3(256), 0,
+                         st, cpart, bcs, N3, (bf16_t*)db_attn);
     }
   } else {
     const float* qkv = (const float*)h->qkv;
@@ -363,8 +363,8 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     if (db_proj) {
       hipLaunchKernelGGL(colsum_partial_kernel<float>, dim3((C + 255) / 256, ncs), dim3(256), 0,
                          st, (const float*)dY, M, C, C, rows_per, cpart);
-      hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3((C + 255) / 256), dim3(256), 0, st,
-                         cpart, ncs, (size_t)C, (size_t)C, (float*)db_proj);
+      hipLaunchKernelGGL(reduce_colparts_kernel<float>, dim3((C + 63) / 64), dim3(256), 0, st,
+                         cpart, ncs, C, (float*)db_proj);
     }
     mark(h, 5, st);
     const dim3 dgrid((unsigned)((M * (long)H + 255) / 256));
@@ -395,8 +395,8 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     if (db_attn) {
       hipLaunchKernelGGL(colsum_partial_kernel<float>, dim3((N3 + 255) / 256, ncs), dim3(256), 0,
                          st, dqkv, M, N3, N3, rows_per, cpart);
-      hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3((N3 + 255) / 256), dim3(256), 0, st,
-                         cpart, ncs, (size_t)N3, (size_t)N3, (float*)db_attn);
+      hipLaunchKernelGGL(reduce_colparts_kernel<float>, dim3((N3 + 63) / 64), dim3(256), 0, st,
+                         cpart, ncs, N3, (float*)db_attn);
     }
   }
   mark(h, 7, st);
