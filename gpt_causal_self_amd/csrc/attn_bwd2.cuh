@@ -26,43 +26,50 @@ namespace gpt_attn {
 
 constexpr float kLog2eB = 1.4426950408889634f;
 
-// Padded per-row statistics for the dK/dV kernel: L2[bh][t] = lse * log2(e)
-// and D[bh][t] = dO_t . o_t, rows of Tpad = T rounded up to 64 (the padding
-// is never used: masked lanes select 0).  One thread per 8 elements of a row
-// of dO and O, the head's lanes summed with lane_group_sum.
+// Epilogue of the c_proj input-gradient GEMM dO = dY W_proj^T that also
+// produces the softmax backward row statistics, so dO is not read back:
+// D[b,h,t] = sum_d dO[b,t,h,d] O[b,t,h,d] over the bf16 dO just rounded and
+// the stored forward output O (fmaf over the 8 values of a 16-byte chunk,
+// then a sum of the HS/8 chunks of a head across the lanes that hold them),
+// and L[b,h,t] = lse * log2(e), both in rows of Tpad = T rounded up to 64
+// (the dK/dV kernel reads whole 64-row tiles; rows past T are never used,
+// their lanes select 0).  The GEMM's staged store loop hands consecutive
+// 16-byte chunks of a row to consecutive lanes, so the HS/8 lanes of an
+// aligned group hold one head.
 template <int HS>
-__global__ __launch_bounds__(256) void attn_bwd_rowstats_kernel(
-    const bf16_t* __restrict__ dO, const bf16_t* __restrict__ O, const float* __restrict__ lse,
-    float* __restrict__ Dpad, float* __restrict__ Lpad, int B, int H, int T, int Tpad) {
-  constexpr int Q = HS / 8;
-  const int C = H * HS, per = C / 8;
-  const long g = (long)blockIdx.x * 256 + threadIdx.x;
-  const long total = (long)B * T * per;
-  const bool ok = g < total;
-  float s = 0.f;
-  long row = 0;
-  int c = 0;
-  if (ok) {
-    row = g / per;
-    c = (int)(g - row * per);
-    const uint4 a = *reinterpret_cast<const uint4*>(dO + row * C + 8 * c);
-    const uint4 o = *reinterpret_cast<const uint4*>(O + row * C + 8 * c);
-    const unsigned wa[4] = {a.x, a.y, a.z, a.w}, wo[4] = {o.x, o.y, o.z, o.w};
+struct Epi2DgradRowStats {
+  bf16_t* out;         // dO [M][ldc]
+  int ldc;             // C
+  const bf16_t* bias;  // NULL (no bias on this product)
+  const bf16_t* O;     // forward attention output [M][ldc]
+  const float* lse;    // [B*H][T]
+  float* Dpad;         // [B*H][Tpad]
+  float* Lpad;         // [B*H][Tpad]
+  int T, H, Tpad;
+  static constexpr bool kStaged = true;
+  static constexpr bool kStore8All = true;
+  __device__ __forceinline__ const bf16_t* bias_ptr() const { return bias; }
+  __device__ __forceinline__ void store8_all(int m, int n, uint4 w, bool ok, int lane) const {
+    float s = 0.f;
+    if (ok) {
+      *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = w;
+      const uint4 o = *reinterpret_cast<const uint4*>(O + (size_t)m * ldc + n);
+      const unsigned wa[4] = {w.x, w.y, w.z, w.w}, wo[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s = fmaf(bf2f(wa[e] & 0xffff), bf2f(wo[e] & 0xffff), s);
-      s = fmaf(bf2f(wa[e] >> 16), bf2f(wo[e] >> 16), s);
+      for (int e = 0; e < 4; ++e) {
+        s = fmaf(bf2f(wa[e] & 0xffff), bf2f(wo[e] & 0xffff), s);
+        s = fmaf(bf2f(wa[e] >> 16), bf2f(wo[e] >> 16), s);
+      }
+    }
+    s = lane_group_sum<HS / 8>(s);
+    if (ok && (lane & (HS / 8 - 1)) == 0) {
+      const int b = m / T, t = m - b * T, h = n / HS;
+      const size_t bh = (size_t)b * H + h;
+      Dpad[bh * Tpad + t] = s;
+      Lpad[bh * Tpad + t] = lse[bh * T + t] * kLog2eB;
     }
   }
-  s = lane_group_sum<Q>(s);
-  if (ok && c % Q == 0) {
-    const int h = c / Q;
-    const long b = row / T, t = row - b * T;
-    const size_t bh = (size_t)b * H + h;
-    Dpad[bh * Tpad + t] = s;
-    Lpad[bh * Tpad + t] = lse[bh * T + t] * kLog2eB;
-  }
-}
+};
 
 // ---------------------------------------------------------------- dQ
 // One block = 4 waves = 128 queries of one (b, h); wave w owns 32 queries

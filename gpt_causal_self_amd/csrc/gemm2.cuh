@@ -298,6 +298,16 @@ struct Staged { static constexpr bool value = false; };
 template <class Epi>
 struct Staged<Epi, decltype(void(Epi::kStaged))> { static constexpr bool value = Epi::kStaged; };
 
+// kStore8All: the staged epilogue calls store8_all(m, n, w, in_range, lane)
+// from every lane of every wave (with in_range false outside the matrix),
+// so the epilogue may combine values across lanes.
+template <class Epi, class = void>
+struct Store8All { static constexpr bool value = false; };
+template <class Epi>
+struct Store8All<Epi, decltype(void(Epi::kStore8All))> {
+  static constexpr bool value = Epi::kStore8All;
+};
+
 template <class Epi, class = void>
 struct SplitOffsets { static constexpr bool value = false; };
 template <class Epi>
@@ -470,45 +480,52 @@ void gemm2_kernel(
       }
     bar_nofence();
     constexpr int kChunks = BM * BN / 8;
+    static_assert(!Store8All<Epi>::value || kChunks % (64 * NW) == 0,
+                  "store8_all needs every lane in every pass");
     for (int c = tid; c < kChunks; c += 64 * NW) {
       const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
       const int m = m0 + rl, n = n0 + cl;
-      if (m < M && n < N) epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
+      if constexpr (Store8All<Epi>::value)
+        epi.store8_all(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl), m < M && n < N,
+                       lane);
+      else if (m < M && n < N)
+        epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
     }
-    return;
-  }
-  // ---- epilogue straight from the D^T accumulators
+  } else {
+    static_assert(!Store8All<Epi>::value, "store8_all epilogues need the staged path");
+    // ---- epilogue straight from the D^T accumulators
 #pragma unroll
-  for (int i = 0; i < MT; ++i) {
-    const int m = m0 + wm * WTM + i * 32 + (lane & 31);
-    if (m >= M) continue;
-    if constexpr (SplitOffsets<Epi>::value) {
-      const size_t ro = epi.row_off(m);
+    for (int i = 0; i < MT; ++i) {
+      const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+      if (m >= M) continue;
+      if constexpr (SplitOffsets<Epi>::value) {
+        const size_t ro = epi.row_off(m);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int nb = n0 + wn * WTN + j * 32;
-        if (nb >= N) continue;
-        const size_t co = epi.col_off(nb);
+        for (int j = 0; j < NT; ++j) {
+          const int nb = n0 + wn * WTN + j * 32;
+          if (nb >= N) continue;
+          const size_t co = epi.col_off(nb);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int dn = 8 * g + 4 * (lane >> 5);
-          const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                              acc[i][j][4 * g + 3]};
-          epi.store(ro + co + dn, nb + dn, v);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-          if (n < N) {
+          for (int g = 0; g < 4; ++g) {
+            const int dn = 8 * g + 4 * (lane >> 5);
             const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                                 acc[i][j][4 * g + 3]};
-            epi(m, n, v);
+            epi.store(ro + co + dn, nb + dn, v);
           }
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+            if (n < N) {
+              const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                  acc[i][j][4 * g + 3]};
+              epi(m, n, v);
+            }
+          }
+      }
     }
   }
 }

@@ -276,10 +276,20 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
                          0, st, (const bf16_t*)dY, (bf16_t*)h->ln, (long)M, C, dp);
       dY = h->ln;
     }
-    // ---- c_proj: dym = dY W_proj^T ; dW_proj = ym^T dY ; db_proj = colsum(dY)
-    Epi2RowMajor e_dym{dym, C, nullptr};
-    launch_gemm2<GA_DGRAD_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M, C,
-                                            C, e_dym, st);
+    // ---- c_proj: dym = dY W_proj^T (its epilogue also writes the softmax
+    // backward row statistics D and L) ; dW_proj = ym^T dY ; db_proj = colsum(dY)
+    const int Tpad = (T + 63) / 64 * 64;
+    float* Dpad = h->rowstats;
+    float* Lpad = h->rowstats + (size_t)B * H * Tpad;
+    if (hs == 64) {
+      Epi2DgradRowStats<64> e_dym{dym, C, nullptr, o, h->lse, Dpad, Lpad, T, H, Tpad};
+      launch_gemm2<GA_DGRAD_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M,
+                                              C, C, e_dym, st);
+    } else {
+      Epi2DgradRowStats<32> e_dym{dym, C, nullptr, o, h->lse, Dpad, Lpad, T, H, Tpad};
+      launch_gemm2<GA_DGRAD_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M,
+                                              C, C, e_dym, st);
+    }
     Epi2Partial e_wp{part, C, (size_t)C * C};
     const int s1 = splits_for(((C + 127) / 128) * ((C + 127) / 128));
     const int n1 = launch_gemm2<GA_WGRAD_TILE, false, false>(o, C, (const bf16_t*)dY, C, C, C, M,
@@ -297,15 +307,9 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     const bf16_t* q = qkv;
     const bf16_t* k = qkv + head_elems;
     const bf16_t* v = qkv + 2 * head_elems;
-    const dim3 vgrid((unsigned)(((long)M * (C / 8) + 255) / 256));
-    const int Tpad = (T + 63) / 64 * 64;
-    float* Dpad = h->rowstats;
-    float* Lpad = h->rowstats + (size_t)B * H * Tpad;
     const dim3 kgrid2(B * H, (T + 127) / 128);
     const dim3 qgrid2(B * H, (T + 127) / 128);
     if (hs == 64) {
-      hipLaunchKernelGGL(attn_bwd_rowstats_kernel<64>, vgrid, dim3(256), 0, st, dym, o, h->lse,
-                         Dpad, Lpad, B, H, T, Tpad);
       if (drop) {
         hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<64, true>), kgrid2, dim3(256), 0, st, q,
                            k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
@@ -319,8 +323,6 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
                            v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, DropParams{});
       }
     } else {
-      hipLaunchKernelGGL(attn_bwd_rowstats_kernel<32>, vgrid, dim3(256), 0, st, dym, o, h->lse,
-                         Dpad, Lpad, B, H, T, Tpad);
       if (drop) {
         hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<32, true>), kgrid2, dim3(256), 0, st, q,
                            k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
