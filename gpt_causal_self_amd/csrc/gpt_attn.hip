@@ -226,8 +226,11 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
   // bf16 column sums: row slices of about 384 rows (12 rows per thread)
   const int bcs = std::max(1, std::min(kColsumSplits, (M + 383) / 384));
   const int brows = (M + bcs - 1) / bcs;
+  // Split-K factor of a weight-gradient GEMM: as many k-slices as fit the
+  // chip in one pass (two 128x128 blocks per CU on 256 CUs), so no block
+  // waits for a second round.
   auto splits_for = [](int tiles) {
-    int s = (2 * 256 + tiles - 1) / tiles;
+    int s = (2 * 256) / tiles;
     return s < 1 ? 1 : (s > kWgradSplits ? kWgradSplits : s);
   };
   const int rblocks = 1024;
