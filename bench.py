@@ -19,7 +19,10 @@ over `--pmc-run` (FETCH_SIZE, then WRITE_SIZE), each scaled by what the same
 counter reads for a plain device copy of known size launched in the same
 run; `--write-traffic FETCH_DIR WRITE_DIR` turns the two passes into the
 summary under profiles/, which the benchmark reports while the kernel sources
-it was taken from are unchanged (else null).
+it was taken from are unchanged (else null); the forward kernels then also
+carry `hbm_gbs`, those bytes over the kernel's event time.  MFMA, LDS and VALU
+utilisation per kernel come from one more counter pass over `--pmc-run-all`
+(forward, training and MLP steps), summarised by `--write-util PMC_DIR`.
 """
 from __future__ import annotations
 
@@ -205,6 +208,85 @@ def write_traffic(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT "
+                 "SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_VALU_MFMA_COEXEC_CYCLES GRBM_GUI_ACTIVE")
+UTIL_FILE = os.path.join(ROOT, "profiles", "mfma_lds_util_kernels_gpt2_124m_B12_T1024.md")
+SIMD_NUM, CU_NUM, XCD_NUM = 1024, 256, 8   # MI355X: 8 XCDs x 32 CUs x 4 SIMDs
+
+
+def write_util(run_dir):
+    """Per-kernel MFMA / LDS / VALU utilisation from one rocprofv3 --pmc pass
+    over `--pmc-run-all` (forward, training step and MLP at the GPT-2 124M
+    shape).  rocprofv3 reports each counter once per dispatch, summed over
+    the chip; GRBM_GUI_ACTIVE is then the sum of the 8 XCDs' active cycles,
+    so one XCD's (the kernel's duration in cycles) is that sum / 8.  The
+    ratios follow rocprofv3's derived MfmaUtil / LdsUtil / LdsBankConflict
+    / VALUBusy metrics."""
+    import csv
+    import glob
+    import re
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}   # kernel -> dispatch -> counter -> [sum, max]
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            name = re.sub(r"\(.*", "", r["Kernel_Name"]).replace("void ", "")
+            name = name.replace("gpt_attn::", "").replace("unsigned short", "bf16")
+            if "rocclr" in name or "at::native" in name:
+                continue
+            d = r.get("Dispatch_Id", r.get("Correlation_Id"))
+            v = float(r["Counter_Value"])
+            c = per.setdefault(name, {}).setdefault(d, {}).setdefault(r["Counter_Name"], [0.0, 0.0])
+            c[0] += v
+            c[1] = max(c[1], v)
+    lines = ["# MFMA, LDS and VALU utilisation per kernel: GPT-2 124M attention layer "
+             "(B12 T1024 C768 H12 bf16), forward, training step and MLP", "",
+             "Commands (from /tmp with TMPDIR=/tmp on one MI355X; repository at $R):", "", "```",
+             f"timeout -s KILL 60 rocprofv3 --pmc {UTIL_COUNTERS} -f csv -d $R/gpurun_out/pmc_util "
+             "-- python3 $R/bench.py --pmc-run-all",
+             "python3 $R/bench.py --write-util $R/gpurun_out/pmc_util", "```", "",
+             f"Sources digest: {sources_digest()}", "",
+             "Per dispatch, averaged over dispatches, with A = GRBM_GUI_ACTIVE / "
+             f"{XCD_NUM} (the counter sums the XCDs' active cycles): MFMA util = "
+             f"SQ_VALU_MFMA_BUSY_CYCLES / (A x {SIMD_NUM} SIMDs); LDS active and bank-conflict = "
+             f"100 x counter / (A x {CU_NUM} CUs); VALU busy = 100 x SQ_ACTIVE_INST_VALU / "
+             f"{CU_NUM} / A; MFMA+VALU co-issue = 100 x SQ_VALU_MFMA_COEXEC_CYCLES / "
+             f"(A x {SIMD_NUM}); MFMA/VALU instructions are "
+             "wave-level counts per dispatch (a 32x32x16 bf16 MFMA is 32768 FLOP).  Counter "
+             "collection serialises the kernels, so active cycles cover each kernel alone.", "",
+             "| kernel | dispatches | MFMA util % | MFMA instr | VALU instr | VALU busy % | "
+             "MFMA+VALU co-issue % | LDS active % | LDS bank-conflict % |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    rows = []
+    for name, ds in per.items():
+        acc = {}
+        for d in ds.values():
+            for cn, (sm, mx) in d.items():
+                a = acc.setdefault(cn, [0.0, 0.0, 0])
+                a[0] += sm
+                a[1] += mx
+                a[2] += 1
+        mean = {cn: (a[0] / a[2], a[1] / a[2]) for cn, a in acc.items()}
+        if "GRBM_GUI_ACTIVE" not in mean or "SQ_VALU_MFMA_BUSY_CYCLES" not in mean:
+            continue
+        gui = mean["GRBM_GUI_ACTIVE"][0] / XCD_NUM
+        g = lambda cn: mean.get(cn, (0.0, 0.0))[0]
+        rows.append((gui * len(ds), name, len(ds),
+                     100.0 * g("SQ_VALU_MFMA_BUSY_CYCLES") / (gui * SIMD_NUM),
+                     g("SQ_INSTS_MFMA"), g("SQ_INSTS_VALU"),
+                     100.0 * g("SQ_ACTIVE_INST_VALU") / CU_NUM / gui,
+                     100.0 * g("SQ_VALU_MFMA_COEXEC_CYCLES") / (gui * SIMD_NUM),
+                     100.0 * g("SQ_LDS_IDX_ACTIVE") / (gui * CU_NUM),
+                     100.0 * g("SQ_LDS_BANK_CONFLICT") / (gui * CU_NUM)))
+    for r in sorted(rows, reverse=True):
+        lines.append(f"| `{r[1]}` | {r[2]} | {r[3]:.1f} | {r[4]:.0f} | {r[5]:.0f} | {r[6]:.1f} | "
+                     f"{r[7]:.1f} | {r[8]:.1f} | {r[9]:.1f} |")
+    with open(UTIL_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def write_kernel_stats(stats_dir, out_md):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run."""
     import csv
@@ -276,6 +358,45 @@ def pmc_run(steps):
     print(f"pmc run: {steps} forward steps, copy of {COPY_BYTES} bytes", flush=True)
 
 
+def pmc_run_all(steps):
+    """Short run for the utilisation counter pass: forward steps, training
+    steps (forward with saved state + backward) and MLP forwards at the
+    GPT-2 124M shape."""
+    import torch
+    from gpt_causal_self_amd import gpt_attn as ga
+    from gpt_causal_self_amd.inputs import WORKLOADS, make_inputs, to_torch
+    w = WORKLOADS[2]
+    B, T, C, H = w.B, w.T, w.C, w.H
+    dev = torch.device("cuda", 0)
+    inp = make_inputs(B, T, C, H, bias=True, dtype="bf16", seed=125, w_std=w.w_std,
+                      b_attn_std=w.b_attn_std, proj_std=w.proj_std, b_proj_std=w.b_proj_std)
+    t = {k: to_torch(getattr(inp, k), "bf16", dev)
+         for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj")}
+    y = torch.empty_like(t["x"])
+    dY = torch.randn(y.shape, device=dev).to(torch.bfloat16)
+    g = {k: torch.empty_like(t[src]) for k, src in
+         (("dx", "x"), ("dWa", "W_attn"), ("dba", "b_attn"), ("dWp", "W_proj"), ("dbp", "b_proj"))}
+    layer = ga.Layer(C, H, B, T, "bf16")
+    for _ in range(steps):
+        ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"], t["W_proj"],
+                            t["b_proj"], H, y)
+    for _ in range(steps):
+        ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"], t["W_proj"],
+                            t["b_proj"], H, y, save_for_backward=True)
+        ga.gpt_attn_backward(layer.h, t["x"], t["W_attn"], t["W_proj"], dY, g["dx"], g["dWa"],
+                             g["dba"], g["dWp"], g["dbp"])
+    M, F = B * T, 4 * C
+    wfc = (torch.randn(C, F, device=dev) * 0.02).to(torch.bfloat16)
+    bfc = (torch.randn(F, device=dev) * 0.02).to(torch.bfloat16)
+    wp2 = (torch.randn(F, C, device=dev) * 0.02).to(torch.bfloat16)
+    hbuf = torch.empty(M, F, device=dev, dtype=torch.bfloat16)
+    for _ in range(steps):
+        ga.gpt_mlp_forward(t["x"], wfc, bfc, wp2, t["b_proj"], hbuf, y, residual=t["x"])
+    torch.cuda.synchronize()
+    layer.close()
+    print(f"pmc run: {steps} forward, {steps} training and {steps} MLP steps", flush=True)
+
+
 def time_calls(fn, n, warm=3):
     """Mean milliseconds per call of fn (launches on the current stream),
     from torch events around n back-to-back calls."""
@@ -290,6 +411,43 @@ def time_calls(fn, n, warm=3):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / n
+
+
+def other_configs(n=30):
+    """Forward throughput of the layer at the other parity configurations:
+    the tiny fp32 character model (B=8, T=64, C=128, 4 heads), the
+    gpt2-medium shape (B=8, T=1024, C=1024, 16 heads, bf16) and the gpt2-xl
+    shape without biases (B=4, C=1600, 25 heads, bf16) over its ragged
+    sequence lengths.  Each is timed with events around n back-to-back
+    forwards on one input set (inputs resident in HBM)."""
+    import torch
+    from gpt_causal_self_amd import gpt_attn as ga
+    from gpt_causal_self_amd.inputs import WORKLOADS, make_inputs, to_torch
+    res = {}
+    cases = [(1, WORKLOADS[1].T), (3, WORKLOADS[3].T)]
+    cases += [(4, t) for t in WORKLOADS[4].ragged_T]
+    for idx, T in cases:
+        w = WORKLOADS[idx]
+        B, C, H = w.B, w.C, w.H
+        inp = make_inputs(B, T, C, H, bias=w.bias, dtype=w.dtype, seed=124 + idx,
+                          w_std=w.w_std, b_attn_std=w.b_attn_std, proj_std=w.proj_std,
+                          b_proj_std=w.b_proj_std)
+        t = {k: to_torch(getattr(inp, k), w.dtype, "cuda")
+             for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj")}
+        y = torch.empty_like(t["x"])
+        layer = ga.Layer(C, H, B, T, w.dtype)
+        ms = time_calls(lambda: ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"],
+                                                    t["W_proj"], t["b_proj"], H, y), n)
+        layer.close()
+        F = layer_flops(B, T, C)
+        key = f"cfg{idx}" if idx != 4 else f"cfg4_T{T}"
+        res[key] = {"workload": f"B={B} T={T} C={C} H={H} {w.dtype}" +
+                    ("" if w.bias else " no bias"),
+                    "ms": round(ms, 5), "tflops": round(F / (ms * 1e-3) / 1e12, 3),
+                    "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+                    "frac_of_peak": round(F / (ms * 1e-3) / 1e12 /
+                                          (PEAK_BF16_TFLOPS if w.dtype == "bf16" else 157.3), 4)}
+    return res
 
 
 def next_rows(n=50):
@@ -395,6 +553,10 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=12)
     ap.add_argument("--no-next", action="store_true",
                     help="skip the Block-piece timings (LayerNorm, half-block, MLP)")
+    ap.add_argument("--pmc-run-all", action="store_true",
+                    help="forward, training and MLP steps only (for the utilisation counter pass)")
+    ap.add_argument("--write-util", metavar="PMC_DIR",
+                    help="summarise the utilisation counter pass under profiles/")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short forward-only run plus the calibration copy, for counter passes")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -414,6 +576,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.pmc_run_all:
+        pmc_run_all(min(args.steps, 5))
+        return
+    if args.write_util:
+        write_util(args.write_util)
+        return
     if args.pmc_run:
         pmc_run(min(args.steps, 10))
         return
@@ -478,14 +646,16 @@ def main():
     sf = stage_flops(B, T, C)
     sb = stage_bytes(B, T, C, H)
     kernels = {}
+    rec = load_traffic()
     for k in ("c_attn", "attention", "c_proj"):
         kernels[k] = {"ms": round(mean[k], 5),
                       "tflops": round(sf[k] / (mean[k] * 1e-3) / 1e12, 2),
                       "gbs": round(sb[k] / (mean[k] * 1e-3) / 1e9, 1),
                       "flop_per_launch": sf[k], "bytes_per_launch": sb[k]}
+        if rec and k in rec["kernels"]:
+            kernels[k]["hbm_gbs"] = round(rec["kernels"][k]["bytes"] / (mean[k] * 1e-3) / 1e9, 1)
     dom = max(("c_attn", "attention", "c_proj"), key=lambda k: mean[k])
     achieved = sf[dom] / (mean[dom] * 1e-3) / 1e12
-    rec = load_traffic()
     traffic = None
     if rec and dom in rec["kernels"]:
         traffic = round(rec["kernels"][dom]["bytes"])
@@ -544,6 +714,7 @@ def main():
 
     if not args.no_next:
         out["next_rows"] = next_rows()
+        out["other_configs"] = other_configs()
 
     if not args.no_cpu:
         cb = cpu_baseline(2, args.cpu_seqs)

@@ -2,6 +2,8 @@
 // gpt_attn_forward and the Pre-LN block entry point.
 #pragma once
 
+#include <algorithm>
+
 #include "attn_fwd.cuh"
 #include "gemm2.cuh"
 #include "handle.cuh"
@@ -67,6 +69,55 @@ struct Epi2RowMajorDrop {
   }
 };
 
+// Split-K for a projection whose output tiles cannot fill the chip (short
+// sequences: at B = 4, C = 1600 the c_attn GEMM has 19 tiles per 256 rows).
+// The k-slices write fp32 partials [s][M][N] into the handle's partial
+// buffer; splitk_finish_kernel sums them in slice order and hands the sums
+// to the projection's own epilogue (bias, q/k/v scatter, residual, dropout),
+// so the result differs from the single-pass GEMM only in the fp32 order of
+// the k summation.
+template <class Epi>
+__global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restrict__ part,
+                                                            int S, int M, int N, Epi epi) {
+  const int n4 = N / 4;
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long)M * n4) return;
+  const int m = (int)(i / n4), n = (int)(i - (long)m * n4) * 4;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float4 p = *reinterpret_cast<const float4*>(part + ((size_t)s * M + m) * N + n);
+    v[0] += p.x; v[1] += p.y; v[2] += p.z; v[3] += p.w;
+  }
+  if constexpr (SplitOffsets<Epi>::value)
+    epi.store(epi.row_off(m) + epi.col_off(n), n, v);
+  else
+    epi(m, n, v);
+}
+
+// The projection GEMM, split along K when it has fewer than 128 output
+// tiles: up to 8 slices (each at least 2 k-tiles), as many as give about
+// 256 blocks and fit the partial buffer.
+template <int BM, int BN, int NSTAGE, int BK, int WGM, int WGN, bool A_KC, bool B_KC,
+          int OCC = 1, class Epi>
+inline void launch_proj(const gpt_attn_handle* h, const bf16_t* A, int lda, const bf16_t* Bm,
+                        int ldb, int M, int N, int K, const Epi& epi, hipStream_t st) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int nk = (K + BK - 1) / BK;
+  int s = tiles >= 128 ? 1 : std::min(std::min(256 / std::max(tiles, 1), nk / 2), 8);
+  while (s > 1 && (size_t)s * M * N > h->part_elems) --s;
+  if (s <= 1) {
+    launch_gemm2<BM, BN, NSTAGE, BK, WGM, WGN, A_KC, B_KC, OCC>(A, lda, Bm, ldb, M, N, K, epi,
+                                                                st);
+    return;
+  }
+  Epi2Partial ep{h->part, N, (size_t)M * N};
+  const int ns = launch_gemm2<BM, BN, NSTAGE, BK, WGM, WGN, A_KC, B_KC, OCC>(
+      A, lda, Bm, ldb, M, N, K, ep, st, s);
+  const long total = (long)M * (N / 4);
+  hipLaunchKernelGGL(splitk_finish_kernel<Epi>, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, st, (const float*)h->part, ns, M, N, epi);
+}
+
 // c_attn GEMM -> fused causal attention -> c_proj GEMM on stream st.
 // residual == NULL: y = layer(x); else y = residual + layer(x).
 // lse != NULL: also store the softmax log-sum-exp rows for the backward.
@@ -84,7 +135,7 @@ inline void layer_forward_bf16(const gpt_attn_handle* h, const bf16_t* x, int B,
   bf16_t* o = (bf16_t*)h->o;
   Epi2QKV e1{qkv, b_attn, B, T, C, H, hs};
   mark(h, 0, st);
-  launch_gemm2<GA_QKV_TILE, true, false>(x, C, W_attn, 3 * C, M, 3 * C, C, e1, st);
+  launch_proj<GA_QKV_TILE, true, false>(h, x, C, W_attn, 3 * C, M, 3 * C, C, e1, st);
   mark(h, 1, st);
   const dim3 agrid(B * H, (T + kAttnBQ - 1) / kAttnBQ);
   if (drop) {
@@ -108,13 +159,13 @@ inline void layer_forward_bf16(const gpt_attn_handle* h, const bf16_t* x, int B,
   mark(h, 2, st);
   if (drop) {
     Epi2RowMajorDrop e3{y, C, b_proj, residual, *drop};
-    launch_gemm2<GA_PROJ_TILE, true, false>(o, C, W_proj, C, M, C, C, e3, st);
+    launch_proj<GA_PROJ_TILE, true, false>(h, o, C, W_proj, C, M, C, C, e3, st);
   } else if (residual) {
     Epi2RowMajorRes e3{y, C, b_proj, residual};
-    launch_gemm2<GA_PROJ_TILE, true, false>(o, C, W_proj, C, M, C, C, e3, st);
+    launch_proj<GA_PROJ_TILE, true, false>(h, o, C, W_proj, C, M, C, C, e3, st);
   } else {
     Epi2RowMajor e3{y, C, b_proj};
-    launch_gemm2<GA_PROJ_TILE, true, false>(o, C, W_proj, C, M, C, C, e3, st);
+    launch_proj<GA_PROJ_TILE, true, false>(h, o, C, W_proj, C, M, C, C, e3, st);
   }
   mark(h, 3, st);
 }
