@@ -345,59 +345,91 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
 }
 
 // ---------------------------------------------------------------- fp32
+// fp32 path: 64 queries per block, four lanes per query (lane t of a quad
+// holds dimensions [t*HS/4, (t+1)*HS/4) of q and of the output); 64-key
+// K/V tiles in LDS.  Keys go in chunks of 8: the quad's partial dot
+// products meet through two DPP exchanges (all four lanes then hold the same
+// scores), and the online softmax rescales once per chunk.
 template <int HS>
-__global__ __launch_bounds__(64) void attn_fwd_f32_kernel(
+__global__ __launch_bounds__(256) void attn_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ Kg, const float* __restrict__ Vg,
     float* __restrict__ O, float* __restrict__ lse, int H, int T, float scale_log2) {
-  constexpr int BQ = 64, BKV = 64;
-  __shared__ float Ks[BKV][HS];
-  __shared__ float Vs[BKV][HS];
+  constexpr int BQ = 64, BKV = 64, D4 = HS / 4, CH = 8;
+  __shared__ __align__(16) float Ks[BKV][HS];
+  __shared__ __align__(16) float Vs[BKV][HS];
   const int bh = blockIdx.x;
   const int nqt = (T + BQ - 1) / BQ;
   const int qt = nqt - 1 - (int)blockIdx.y;
   const int b = bh / H, h = bh - b * H;
   const size_t head = (size_t)bh * T * HS;
-  const int tid = threadIdx.x;
-  const int myq = qt * BQ + tid;
-  float q[HS], o[HS];
+  const int tid = threadIdx.x, sub = tid & 3;
+  const int myq = qt * BQ + (tid >> 2);
+  float q[D4], o[D4];
 #pragma unroll
-  for (int d = 0; d < HS; ++d) {
-    q[d] = (myq < T) ? Q[head + (size_t)myq * HS + d] : 0.f;
-    o[d] = 0.f;
+  for (int d = 0; d < D4; d += 4) {
+    const float4 v = myq < T ? *reinterpret_cast<const float4*>(Q + head + (size_t)myq * HS +
+                                                                sub * D4 + d)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
+    q[d] = v.x; q[d + 1] = v.y; q[d + 2] = v.z; q[d + 3] = v.w;
+    o[d] = o[d + 1] = o[d + 2] = o[d + 3] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
   const int kv_end = min(T, (qt + 1) * BQ);
   for (int j0 = 0; j0 < kv_end; j0 += BKV) {
     __syncthreads();
-    for (int e = tid; e < BKV * HS; e += 64) {
-      const int key = e / HS, d = e % HS;
+    for (int e = tid; e < BKV * HS / 4; e += 256) {
+      const int key = e / (HS / 4), d = (e % (HS / 4)) * 4;
       const bool ok = j0 + key < T;
-      Ks[key][d] = ok ? Kg[head + (size_t)(j0 + key) * HS + d] : 0.f;
-      Vs[key][d] = ok ? Vg[head + (size_t)(j0 + key) * HS + d] : 0.f;
+      const size_t g = head + (size_t)(j0 + key) * HS + d;
+      *reinterpret_cast<float4*>(&Ks[key][d]) =
+          ok ? *reinterpret_cast<const float4*>(Kg + g) : make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(&Vs[key][d]) =
+          ok ? *reinterpret_cast<const float4*>(Vg + g) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();
-    const int jmax = min(BKV, min(kv_end, myq + 1) - j0);  // keys j0 .. j0+jmax-1 visible
-    for (int jj = 0; jj < jmax; ++jj) {
-      float dot = 0.f;
+    // keys j0 .. j0+jmax-1 are visible to this query (same for the quad)
+    const int jmax = max(0, min(BKV, min(kv_end, myq + 1) - j0));
+    for (int c0 = 0; c0 < jmax; c0 += CH) {
+      float t[CH];
 #pragma unroll
-      for (int d = 0; d < HS; ++d) dot = fmaf(q[d], Ks[jj][d], dot);
-      const float t = dot * scale_log2;
-      const float m_new = fmaxf(m, t);
+      for (int k = 0; k < CH; ++k) {
+        const float* kr = &Ks[c0 + k][sub * D4];
+        float dot = 0.f;
+#pragma unroll
+        for (int d = 0; d < D4; ++d) dot = fmaf(q[d], kr[d], dot);
+        dot += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dot), 0xB1, 0xF, 0xF, false));
+        dot += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(dot), 0x4E, 0xF, 0xF, false));
+        t[k] = c0 + k < jmax ? dot * scale_log2 : -INFINITY;
+      }
+      float cmax = t[0];
+#pragma unroll
+      for (int k = 1; k < CH; ++k) cmax = fmaxf(cmax, t[k]);
+      const float m_new = fmaxf(m, cmax);  // finite: key c0 is visible
       const float alpha = __builtin_amdgcn_exp2f(m - m_new);
-      const float p = __builtin_amdgcn_exp2f(t - m_new);
-      l = l * alpha + p;
+      l *= alpha;
 #pragma unroll
-      for (int d = 0; d < HS; ++d) o[d] = fmaf(p, Vs[jj][d], o[d] * alpha);
+      for (int d = 0; d < D4; ++d) o[d] *= alpha;
+#pragma unroll
+      for (int k = 0; k < CH; ++k) {
+        const float p = c0 + k < jmax ? __builtin_amdgcn_exp2f(t[k] - m_new) : 0.f;
+        l += p;
+        const float* vr = &Vs[c0 + k][sub * D4];
+#pragma unroll
+        for (int d = 0; d < D4; ++d) o[d] = fmaf(p, vr[d], o[d]);
+      }
       m = m_new;
     }
   }
   if (myq < T) {
     const int C = HS * H;
     const float inv = 1.f / l;
-    float* orow = O + ((size_t)b * T + myq) * C + h * HS;
+    float* orow = O + ((size_t)b * T + myq) * C + h * HS + sub * D4;
 #pragma unroll
-    for (int d = 0; d < HS; ++d) orow[d] = o[d] * inv;
-    if (lse != nullptr) lse[(size_t)bh * T + myq] = (m + __log2f(l)) * 0.69314718055994530942f;
+    for (int d = 0; d < D4; d += 4)
+      *reinterpret_cast<float4*>(orow + d) =
+          make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv);
+    if (lse != nullptr && sub == 0)
+      lse[(size_t)bh * T + myq] = (m + __log2f(l)) * 0.69314718055994530942f;
   }
 }
 

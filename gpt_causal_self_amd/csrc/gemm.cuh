@@ -308,43 +308,71 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(
 }
 
 // ============================================================ fp32 FMA
+// 64 x 64 tile, 16 x 16 threads with 4 x 4 outputs each, BK = 32.  The next
+// k-tile's global loads are issued into registers before the current tile's
+// FMAs and land in the other half of a double-buffered LDS tile, so each
+// step waits for its loads only after a tile of arithmetic and needs one
+// barrier.  Consecutive threads load consecutive addresses: along k for a
+// k-contiguous operand, along the rows otherwise.
 template <bool A_KC, bool B_KC, class Epi>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(
     const float* __restrict__ A, int lda, const float* __restrict__ Bm, int ldb, int M,
     int N, int K, Epi epi) {
-  constexpr int BM = 64, BN = 64, BK = 16;
-  __shared__ float As[BK][BM + 4];
-  __shared__ float Bs[BK][BN + 4];
+  constexpr int BM = 64, BN = 64, BK = 32;
+  constexpr int PER = BK * BM / 256;  // elements of each operand per thread per k-tile
+  __shared__ float As[2][BK][BM + 4];
+  __shared__ float Bs[2][BK][BN + 4];
   const int tiles_n = (N + BN - 1) / BN;
   const int m0 = (blockIdx.x / tiles_n) * BM, n0 = (blockIdx.x % tiles_n) * BN;
   const int tid = threadIdx.x;
-  const int tm = tid / 16, tn = tid % 16;  // 16 x 16 threads, 4 x 4 outputs each
+  const int tm = tid / 16, tn = tid % 16;
   float acc[4][4] = {};
+  float ra[PER], rb[PER];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i;
+      const int ka = A_KC ? e % BK : e / BM, ma = A_KC ? e / BK : e % BM;
+      const int kb = B_KC ? e % BK : e / BN, nb = B_KC ? e / BK : e % BN;
+      const int gm = m0 + ma, gka = k0 + ka, gn = n0 + nb, gkb = k0 + kb;
+      ra[i] = (gm < M && gka < K) ? (A_KC ? A[(size_t)gm * lda + gka] : A[(size_t)gka * lda + gm])
+                                  : 0.f;
+      rb[i] = (gn < N && gkb < K) ? (B_KC ? Bm[(size_t)gn * ldb + gkb] : Bm[(size_t)gkb * ldb + gn])
+                                  : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = tid + 256 * i;
+      if (A_KC) As[buf][e % BK][e / BK] = ra[i];
+      else As[buf][e / BM][e % BM] = ra[i];
+      if (B_KC) Bs[buf][e % BK][e / BK] = rb[i];
+      else Bs[buf][e / BN][e % BN] = rb[i];
+    }
+  };
+  load(0);
+  store(0);
+  __syncthreads();
+  int buf = 0;
   for (int k0 = 0; k0 < K; k0 += BK) {
-    for (int e = tid; e < BK * BM; e += 256) {
-      const int kk = e / BM, mm = e % BM;
-      const int gm = m0 + mm, gk = k0 + kk;
-      As[kk][mm] = (gm < M && gk < K) ? (A_KC ? A[(size_t)gm * lda + gk] : A[(size_t)gk * lda + gm]) : 0.f;
-    }
-    for (int e = tid; e < BK * BN; e += 256) {
-      const int kk = e / BN, nn = e % BN;
-      const int gn = n0 + nn, gk = k0 + kk;
-      Bs[kk][nn] = (gn < N && gk < K) ? (B_KC ? Bm[(size_t)gn * ldb + gk] : Bm[(size_t)gk * ldb + gn]) : 0.f;
-    }
-    __syncthreads();
+    const bool next = k0 + BK < K;
+    if (next) load(k0 + BK);
 #pragma unroll
     for (int kk = 0; kk < BK; ++kk) {
       float a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][tm * 4 + i];
+      for (int i = 0; i < 4; ++i) a[i] = As[buf][kk][tm * 4 + i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tn * 4 + j];
+      for (int j = 0; j < 4; ++j) b[j] = Bs[buf][kk][tn * 4 + j];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
+    if (next) store(buf ^ 1);
     __syncthreads();
+    buf ^= 1;
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)

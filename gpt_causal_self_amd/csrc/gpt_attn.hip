@@ -168,10 +168,10 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
     mark(h, 1, st);
     const dim3 agrid(B * H, (T + 63) / 64);
     if (hs == 64)
-      hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, agrid, dim3(64), 0, st, qkv,
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, agrid, dim3(256), 0, st, qkv,
                          qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
     else
-      hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, agrid, dim3(64), 0, st, qkv,
+      hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, agrid, dim3(256), 0, st, qkv,
                          qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2);
     mark(h, 2, st);
     EpiRowMajor<float> e3{(float*)y, C, (const float*)b_proj};
