@@ -361,6 +361,57 @@ __device__ __forceinline__ void g2_step(const char* __restrict__ rd, char* __res
   }
 }
 
+// Staged epilogue: bias (read from the tile's bias columns at LDS offset
+// bias_off), activation and bf16 rounding into an LDS tile [BM][BN+8] that
+// reuses the operand ring, then every 8 lanes store one 128-byte run of a row.
+// Wave (wm, wn) holds the (BM/WGM) x (BN/WGN) sub-tile of D^T accumulators.
+template <int BM, int BN, int WGM, int WGN, class Epi>
+__device__ __forceinline__ void g2_store_staged(char* smem, int bias_off,
+                                                const floatx16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                                const Epi& epi, int m0, int n0, int M, int N,
+                                                int tid, int wm, int wn) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MT = WTM / 32, NT = WTN / 32;
+  const int lane = tid & 63;
+  constexpr int SP = BN + 8;  // pitch (elements); 16-byte aligned rows
+  bf16_t* ct = reinterpret_cast<bf16_t*>(smem);
+  bar_nofence();  // every wave is done with the operand ring
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int cl = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);  // local column
+      const uint2 bu = *reinterpret_cast<const uint2*>(smem + bias_off + cl * 2);
+      const float b[4] = {bf2f(bu.x & 0xffff), bf2f(bu.x >> 16), bf2f(bu.y & 0xffff),
+                          bf2f(bu.y >> 16)};
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int rl = wm * WTM + i * 32 + (lane & 31);
+        uint2 w;
+        constexpr int ACT = ActOf<Epi>::value;
+        w.x = pack_bf16x2(apply_act<ACT>(acc[i][j][4 * g] + b[0]),
+                          apply_act<ACT>(acc[i][j][4 * g + 1] + b[1]));
+        w.y = pack_bf16x2(apply_act<ACT>(acc[i][j][4 * g + 2] + b[2]),
+                          apply_act<ACT>(acc[i][j][4 * g + 3] + b[3]));
+        *reinterpret_cast<uint2*>(ct + rl * SP + cl) = w;
+      }
+    }
+  bar_nofence();
+  constexpr int kChunks = BM * BN / 8;
+  static_assert(!Store8All<Epi>::value || kChunks % (64 * NW) == 0,
+                "store8_all needs every lane in every pass");
+  for (int c = tid; c < kChunks; c += 64 * NW) {
+    const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+    const int m = m0 + rl, n = n0 + cl;
+    if constexpr (Store8All<Epi>::value)
+      epi.store8_all(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl), m < M && n < N,
+                     lane);
+    else if (m < M && n < N)
+      epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
+  }
+}
+
 // OCC: waves per SIMD the register allocation must allow (1 = no limit
 // beyond the block size).
 template <int BM, int BN, int BK, int NSTAGE, bool A_KC, bool B_KC, int WGM, int WGN, class Epi,
@@ -453,44 +504,7 @@ void gemm2_kernel(
   }
 
   if constexpr (kStagedEpi) {
-    // ---- staged epilogue: bias + bf16 rounding into an LDS tile [BM][BN+8],
-    // then every 8 lanes store one 128-byte run of a row.
-    constexpr int SP = BN + 8;  // pitch (elements); 16-byte aligned rows
-    bf16_t* ct = reinterpret_cast<bf16_t*>(smem);
-    bar_nofence();  // every wave is done with the operand ring
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int cl = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);  // local column
-        const uint2 bu = *reinterpret_cast<const uint2*>(smem + kBiasOff + cl * 2);
-        const float b[4] = {bf2f(bu.x & 0xffff), bf2f(bu.x >> 16), bf2f(bu.y & 0xffff),
-                            bf2f(bu.y >> 16)};
-#pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          const int rl = wm * WTM + i * 32 + (lane & 31);
-          uint2 w;
-          constexpr int ACT = ActOf<Epi>::value;
-          w.x = pack_bf16x2(apply_act<ACT>(acc[i][j][4 * g] + b[0]),
-                            apply_act<ACT>(acc[i][j][4 * g + 1] + b[1]));
-          w.y = pack_bf16x2(apply_act<ACT>(acc[i][j][4 * g + 2] + b[2]),
-                            apply_act<ACT>(acc[i][j][4 * g + 3] + b[3]));
-          *reinterpret_cast<uint2*>(ct + rl * SP + cl) = w;
-        }
-      }
-    bar_nofence();
-    constexpr int kChunks = BM * BN / 8;
-    static_assert(!Store8All<Epi>::value || kChunks % (64 * NW) == 0,
-                  "store8_all needs every lane in every pass");
-    for (int c = tid; c < kChunks; c += 64 * NW) {
-      const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
-      const int m = m0 + rl, n = n0 + cl;
-      if constexpr (Store8All<Epi>::value)
-        epi.store8_all(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl), m < M && n < N,
-                       lane);
-      else if (m < M && n < N)
-        epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
-    }
+    g2_store_staged<BM, BN, WGM, WGN>(smem, kBiasOff, acc, epi, m0, n0, M, N, tid, wm, wn);
   } else {
     static_assert(!Store8All<Epi>::value, "store8_all epilogues need the staged path");
     // ---- epilogue straight from the D^T accumulators
