@@ -315,6 +315,33 @@ def write_kernel_stats(stats_dir, out_md):
         lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['Percentage']):.1f} |")
+    # The table above is rocprofv3's per-name summary over the whole run, in
+    # which the other configurations (other shapes, same kernels) mix in.
+    # The forward kernels at this workload, from the per-dispatch trace,
+    # selected by name and grid (work-items):
+    traces = glob.glob(os.path.join(stats_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if traces:
+        B, T, C, H = 12, 1024, 768, 12
+        M = B * T
+        want = {"c_attn": ("Epi2QKV", (M // 256) * (3 * C // 256) * 512, 1),
+                "attention": ("attn_fwd2_bf16_kernel<64, 2, false>", B * H * 256, T // 128),
+                "c_proj": ("gemm2_kernel<192, 256, 64, 2, true, false, 2, 4, "
+                           "gpt_attn::Epi2RowMajor, 1>", (M // 192) * (C // 256) * 512, 1)}
+        durs = {k: [] for k in want}
+        for r in csv.DictReader(open(traces[0])):
+            for k, (name, gx, gy) in want.items():
+                if (name in r["Kernel_Name"] and int(r["Grid_Size_X"]) == gx
+                        and int(r["Grid_Size_Y"]) == gy):
+                    durs[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += ["", "Forward kernels at this workload (B=12 T=1024 C=768 H=12), from the "
+                  "per-dispatch trace (`*kernel_trace.csv`), selected by kernel and grid size:", "",
+                  "| stage | grid (work-items) | dispatches | avg us | min us | max us |",
+                  "|---|---|---|---|---|---|"]
+        for k, (name, gx, gy) in want.items():
+            d = durs[k]
+            if d:
+                lines.append(f"| {k} | {gx} x {gy} | {len(d)} | {sum(d) / len(d):.1f} | "
+                             f"{min(d):.1f} | {max(d):.1f} |")
     with open(os.path.join(ROOT, "profiles", os.path.basename(out_md)), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
