@@ -10,24 +10,68 @@
 // values of positions 0..pos-1 from a cache: this file computes that step.
 //
 //   skinny_gemm_kernel   out[b][n] = sum_c x[b][c] W[c][n] (+ bias) for a
-//                        handful of rows b (the batch); HBM-bound on W.  The
-//                        epilogue either scatters q / k / v (q to a buffer,
-//                        k and v into the caches at `pos`) or writes a
-//                        row-major output.
-//   decode_attn_kernel   per (b, h) and chunk of kChunk cached keys: scores,
-//                        chunk max, exp2 weights, chunk sum and the weighted
-//                        value sum (fp32 partials); HBM-bound on the cache.
-//   decode_combine_kernel  merges the chunk partials (rescaling by the chunk
-//                        maxima) and writes the merged heads in bf16.
+//                        handful of rows b (the batch); HBM-bound on W.  A
+//                        block takes 16 columns over all rows c and applies
+//                        the epilogue itself, which either scatters q / k / v
+//                        (q to a buffer, k and v into the caches at `pos`) or
+//                        writes a row-major output.
+//   decode_attn_kernel   per (b, h) and chunk of 128 cached keys per wave:
+//                        scores, max, exp2 weights, sum and the weighted
+//                        value sum; HBM-bound on the cache.  With one chunk
+//                        (pos + 1 <= chunk) the block writes the head; with
+//                        more, each block leaves fp32 partials and the last
+//                        chunk block of the (b, h) to finish merges them
+//                        (rescaling by the chunk maxima).
+//
+// Each kernel's work is one dependent chain of memory accesses (loads, a
+// block-local reduction, stores): a decode step is three such launches.
+//
+// "Last block to finish": each block writes its partials with device-scope
+// stores, waits for them, and increments an arrival counter; the block that
+// sees the count reach the number of blocks reads every block's partials with
+// device-scope loads in a fixed order (deterministic results) and resets the
+// counter to zero for the next launch.
 #pragma once
 
 #include "common.cuh"
 
 namespace gpt_attn {
 
-constexpr int kDecChunk = 256;   // cached keys per attention block
 constexpr int kDecMaxB = 16;     // rows of one decode call
-constexpr int kDecCols = 64;     // output columns per skinny-GEMM block
+constexpr int kDecCols = 16;     // output columns per skinny-GEMM block
+
+// Device-scope accesses of the fp32 partials that one block writes and the
+// last block of its group reads back.  Relaxed atomics at agent scope are
+// plain loads and stores marked coherent across the XCDs' L2 caches, so the
+// hand-off needs no whole-cache write-back or invalidation: each thread
+// waits until its partial stores have completed (vmcnt(0)) before the block
+// barrier that precedes the arrival count, and the last block reads the
+// partials with device-scope loads after the count.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0), other counters untouched (gfx9 encoding)
+__device__ __forceinline__ void wait_stores() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+}
+// Arrival count of a block of the group whose counter is *c, out of n
+// blocks: true in the block that arrives last (which also resets *c).
+__device__ __forceinline__ bool arrive_last(unsigned* c, unsigned n, int* flag) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = old == n - 1;
+    if (old == n - 1) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *flag != 0;
+}
 
 // q/k/v epilogue of the decode projection: column n of row b goes to
 // q[b][n] (n < C), k_cache[b][h][pos][d] (C <= n < 2C) or v_cache (2C <= n).
@@ -54,77 +98,81 @@ struct DecRowOut {
   }
 };
 
-// partial[y][b][n] = sum_{c in slice y} x[b][c] W[c][n] for b < B (<=
-// kDecMaxB), n in this block's kDecCols columns, the K rows split into
-// gridDim.y slices (skinny_finish_kernel adds the slices, the bias and
-// applies the epilogue).  512 threads = 8 waves; in a wave
-// lane = ks + 8 * cg: cg picks 8 consecutive columns (16-byte loads; the 8
-// lanes of one ks read one 128-byte row run) and the row slot r = 8 * w + ks
-// takes the rows c = r, r + 64, ...; loads are issued kDecUnroll rows at a
-// time so that several are in flight per lane.  Partial sums are reduced
-// across the 8 row slots of a wave with DPP lane moves and across the 8 waves
-// in LDS (fixed order: the result is deterministic).  x is staged in LDS as
-// bf16.
-constexpr int kDecWaves = 8;
-constexpr int kDecUnroll = 8;
-constexpr int kDecKSplit = 4;   // row slices of a decode projection
+// out.put(b, n, sum_c x[b][c] W[c][n] + bias[n]) for b < B (<= kDecMaxB) and
+// the block's kDecCols = 16 columns n.  512 threads = 8 waves; in a wave lane
+// = ks + 32 * cg: cg picks 8 consecutive columns (one 16-byte load per row)
+// and the row slot r = 32 * w + ks takes the rows c = r, r + 256, ...; up to
+// kDecUnroll of a lane's rows are loaded at once, the first batch before x
+// is staged in LDS (bf16), so that the two loads overlap.  Sums are reduced
+// over the 16 row slots of a 16-lane row with DPP moves and then over the
+// 16 rows of a column group (2 per wave) from LDS, in a fixed order: the
+// result is deterministic.
+#ifndef GA_DEC_WAVES
+#define GA_DEC_WAVES 8
+#endif
+constexpr int kDecWaves = GA_DEC_WAVES;
+constexpr int kDecRowSlots = 32 * kDecWaves;  // rows in flight per pass
+constexpr int kDecUnroll = 8;                 // passes loaded together
 
+template <class Out>
 __global__ __launch_bounds__(64 * kDecWaves) void skinny_gemm_kernel(
     const bf16_t* __restrict__ x, int B, int K, const bf16_t* __restrict__ W, int N,
-    float* __restrict__ partial) {
+    const bf16_t* __restrict__ bias, Out out) {
   extern __shared__ float dsm[];
-  float* red = dsm;                                                   // [8][B][kDecCols]
-  bf16_t* xs = reinterpret_cast<bf16_t*>(dsm + kDecWaves * B * kDecCols);  // [B][K], 16-B aligned
+  float* red = dsm;                                         // [kDecWaves * 4][B][8]
+  bf16_t* xs = reinterpret_cast<bf16_t*>(dsm + kDecWaves * 4 * B * 8);  // [B][K], 16-B aligned
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int ks = lane & 31, cg = lane >> 5;
+  const int n = blockIdx.x * kDecCols + 8 * cg;
+  const int r0 = 32 * w + ks;
+  constexpr int kStep = kDecRowSlots * kDecUnroll;
+  auto load_rows = [&](int cb, uint4 (&u)[kDecUnroll]) {
+#pragma unroll
+    for (int q = 0; q < kDecUnroll; ++q) {
+      const int c = cb + q * kDecRowSlots;
+      u[q] = (n < N && c < K) ? *reinterpret_cast<const uint4*>(W + (size_t)c * N + n)
+                              : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  uint4 u[kDecUnroll];
+  load_rows(r0, u);
   for (int i = tid; i < B * K / 8; i += 64 * kDecWaves)  // K % 8 == 0: 16-byte chunks
     reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
   __syncthreads();
-  const int ks = lane & 7, cg = lane >> 3;
-  const int n = blockIdx.x * kDecCols + 8 * cg;
-  constexpr int kSlots = 8 * kDecWaves;
   float acc[kDecMaxB][8];
 #pragma unroll
   for (int b = 0; b < kDecMaxB; ++b)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
-  // this block's slice of the rows: [kb, ke)
-  const int KS = gridDim.y;
-  const int kb = (int)(((long)K * blockIdx.y) / KS), ke = (int)(((long)K * (blockIdx.y + 1)) / KS);
-  if (n < N) {
-    for (int c0 = kb + 8 * w + ks; c0 < ke; c0 += kSlots * kDecUnroll) {
-      uint4 u[kDecUnroll];
+  auto fma_rows = [&](int cb, const uint4 (&uu)[kDecUnroll]) {
 #pragma unroll
-      for (int q = 0; q < kDecUnroll; ++q) {
-        const int c = c0 + q * kSlots;
-        u[q] = c < ke ? *reinterpret_cast<const uint4*>(W + (size_t)c * N + n)
-                      : make_uint4(0u, 0u, 0u, 0u);
+    for (int q = 0; q < kDecUnroll; ++q) {
+      const int c = cb + q * kDecRowSlots;
+      if (c >= K) break;
+      const unsigned wd[4] = {uu[q].x, uu[q].y, uu[q].z, uu[q].w};
+      float wf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wf[2 * e] = bf2f(wd[e] & 0xffff);
+        wf[2 * e + 1] = bf2f(wd[e] >> 16);
       }
 #pragma unroll
-      for (int q = 0; q < kDecUnroll; ++q) {
-        const int c = c0 + q * kSlots;
-        if (c >= ke) break;
-        const unsigned wd[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-        float wf[8];
+      for (int b = 0; b < kDecMaxB; ++b) {
+        if (b < B) {
+          const float xv = bf2f(xs[b * K + c]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wf[2 * e] = bf2f(wd[e] & 0xffff);
-          wf[2 * e + 1] = bf2f(wd[e] >> 16);
-        }
-#pragma unroll
-        for (int b = 0; b < kDecMaxB; ++b) {
-          if (b < B) {
-            const float xv = bf2f(xs[b * K + c]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(xv, wf[e], acc[b][e]);
-          }
+          for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(xv, wf[e], acc[b][e]);
         }
       }
     }
+  };
+  fma_rows(r0, u);
+  for (int cb = r0 + kStep; cb < K; cb += kStep) {
+    load_rows(cb, u);
+    fma_rows(cb, u);
   }
-  // sum over the 8 row slots of a column group (8 consecutive lanes) with
-  // DPP moves: swap neighbours, swap pairs (every lane of a quad then holds
-  // the quad's sum), then add the mirrored lane of the half-row (the other
-  // quad): every lane of the group ends with the group's total
+  // sum over the 16 lanes of a DPP row: swap neighbours, swap pairs, mirror
+  // the half-row, mirror the row; every lane of the row then holds its total
 #pragma unroll
   for (int b = 0; b < kDecMaxB; ++b) {
     if (b < B) {
@@ -134,123 +182,124 @@ __global__ __launch_bounds__(64 * kDecWaves) void skinny_gemm_kernel(
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
         v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
         acc[b][e] = v;
       }
     }
   }
-  if (ks == 0) {
+  // rows 0, 1 of the wave hold column group 0, rows 2, 3 group 1
+  if ((lane & 15) == 0) {
+    const int row = w * 4 + (lane >> 4);
 #pragma unroll
     for (int b = 0; b < kDecMaxB; ++b)  // unrolled: acc stays in registers
       if (b < B)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) red[((size_t)w * B + b) * kDecCols + 8 * cg + e] = acc[b][e];
+        for (int e = 0; e < 8; ++e) red[((size_t)row * B + b) * 8 + e] = acc[b][e];
   }
   __syncthreads();
-  // this slice's totals -> partial[slice][b][n]
   for (int i = tid; i < B * kDecCols; i += 64 * kDecWaves) {
     const int b = i / kDecCols, col = i - b * kDecCols;
     const int nn = blockIdx.x * kDecCols + col;
     if (nn >= N) continue;
+    const int g = col >> 3, e = col & 7;
     float v = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) v += red[(ww * B + b) * kDecCols + col];
-    partial[((size_t)blockIdx.y * B + b) * N + nn] = v;
+    for (int ww = 0; ww < kDecWaves; ++ww)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) v += red[((size_t)(ww * 4 + 2 * g + h) * B + b) * 8 + e];
+    if (bias) v += bf2f(bias[nn]);
+    out.put(b, nn, v);
   }
 }
 
-// out.put(b, n, sum_y partial[y][b][n] + bias[n]): the fixed-order sum of the
-// row slices of skinny_gemm_kernel (deterministic), one thread per output.
-template <class Out>
-__global__ __launch_bounds__(256) void skinny_finish_kernel(const float* __restrict__ partial,
-                                                            int KS, int B, int N,
-                                                            const bf16_t* __restrict__ bias,
-                                                            Out out) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= B * N) return;
-  const int b = i / N, n = i - b * N;
-  float v = 0.f;
-  for (int y = 0; y < KS; ++y) v += partial[((size_t)y * B + b) * N + n];
-  if (bias) v += bf2f(bias[n]);
-  out.put(b, n, v);
-}
-
-// Attention of one query per (b, h) over cached keys [chunk * kDecChunk,
-// min(pos + 1, (chunk + 1) * kDecChunk)).  One thread per key for the scores;
-// the weighted value sum gives each thread 8 value columns of a few keys.  Writes (m, l, o[0..HS)) in fp32, with
-// m the chunk's max of the log2-scaled scores, l = sum 2^(s - m) and
-// o = sum 2^(s - m) v.
-template <int HS>
-__global__ __launch_bounds__(256) void decode_attn_kernel(const bf16_t* __restrict__ q,
-                                                          const bf16_t* __restrict__ k_cache,
-                                                          const bf16_t* __restrict__ v_cache,
-                                                          float* __restrict__ part, int H,
-                                                          int cache_T, int pos, int nchunk,
-                                                          float scale_log2) {
-  __shared__ float ps[kDecChunk];
-  __shared__ float wred[8];
-  __shared__ float ored[256 / (HS / 8)][HS];
+// Attention of one query per (b, h) over cached keys [chunk * CHUNK,
+// min(pos + 1, (chunk + 1) * CHUNK)), CHUNK = 128 keys per wave of the NT
+// threads.  Each wave takes 128
+// consecutive keys and runs on its own as its loads arrive: lane l scores
+// keys l and l + 64, the wave takes its max, exp2 weights and sum, passes
+// the weights through its own LDS slice, and for the weighted value sum lane
+// l takes 8 value columns (dg) of a group of consecutive keys (kg); the
+// groups are summed with lane shuffles.  The 8 waves' (m, l, o) then merge
+// after the block's one barrier, each rescaled to the common maximum.  One
+// chunk: the block writes y_m[b][h*HS + d] = bf16(o / l).  Several: it writes
+// (m, l, o[0..HS)) in fp32 (m the chunk's max of the log2-scaled scores,
+// l = sum 2^(s - m), o = sum 2^(s - m) v), and the last chunk block of the
+// (b, h) to finish merges the chunks the same way.
+template <int HS, int NT>
+__global__ __launch_bounds__(NT) void decode_attn_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
+    const bf16_t* __restrict__ v_cache, float* __restrict__ part, bf16_t* __restrict__ ym, int H,
+    int cache_T, int pos, int nchunk, float scale_log2, unsigned* __restrict__ counters) {
+  constexpr int NW = NT / 64;
+  constexpr int KPW = 128;                  // keys per wave
+  constexpr int CHUNK = NW * KPW;           // keys per block
+  constexpr int DG = HS / 8, KG = 64 / DG;  // value columns / key groups per wave
+  constexpr int KPG = KPW / KG;             // keys per group
+  __shared__ float ps[NW][KPW];
+  __shared__ float wpart[NW][HS + 2];
+  __shared__ int is_last;
   const int bh = blockIdx.x, chunk = blockIdx.y;
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int C = H * HS;
-  float qf[HS];
-#pragma unroll
-  for (int d8 = 0; d8 < HS / 8; ++d8) {
-    const uint4 u = *reinterpret_cast<const uint4*>(q + (size_t)b * C + h * HS + 8 * d8);
-    const unsigned wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qf[8 * d8 + 2 * e] = bf2f(wd[e] & 0xffff);
-      qf[8 * d8 + 2 * e + 1] = bf2f(wd[e] >> 16);
-    }
-  }
   const size_t head = ((size_t)b * H + h) * cache_T * HS;
-  const int j = chunk * kDecChunk + tid;
-  float s = -INFINITY;
-  if (j <= pos) {
-    const bf16_t* kr = k_cache + head + (size_t)j * HS;
-    float acc = 0.f;
-#pragma unroll
-    for (int d8 = 0; d8 < HS / 8; ++d8) {
-      const uint4 u = *reinterpret_cast<const uint4*>(kr + 8 * d8);
-      const unsigned wd[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(qf[8 * d8 + 2 * e], bf2f(wd[e] & 0xffff), acc);
-        acc = fmaf(qf[8 * d8 + 2 * e + 1], bf2f(wd[e] >> 16), acc);
-      }
-    }
-    s = acc * scale_log2;
-  }
-  float m = s;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  if (lane == 0) wred[w] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-  const float p = j <= pos ? __builtin_amdgcn_exp2f(s - m) : 0.f;
-  ps[tid] = p;
-  float l = p;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-  if (lane == 0) wred[4 + w] = l;
-  __syncthreads();
-  l = wred[4] + wred[5] + wred[6] + wred[7];
-  // weighted value sum: thread -> (key group kg, 8 value columns dg); each
-  // thread reads its group's value rows with 16-byte loads, all in flight
-  constexpr int DG = HS / 8, KG = 256 / DG, KPG = kDecChunk / KG;
-  const int dg = tid % DG, kg = tid / DG;
-  const int jb = chunk * kDecChunk + kg * KPG;
+  const int kw0 = chunk * CHUNK + w * KPW;  // this wave's first key
+  const int dg = lane % DG, kg = lane / DG;
+  const int jb = kw0 + kg * KPG;
   uint4 vr[KPG];
 #pragma unroll
   for (int u = 0; u < KPG; ++u)
     vr[u] = jb + u <= pos
                 ? *reinterpret_cast<const uint4*>(v_cache + head + (size_t)(jb + u) * HS + 8 * dg)
                 : make_uint4(0u, 0u, 0u, 0u);
+  uint4 kr[2][HS / 8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = kw0 + lane + 64 * t;
+#pragma unroll
+    for (int d8 = 0; d8 < HS / 8; ++d8)
+      kr[t][d8] = j <= pos
+                      ? *reinterpret_cast<const uint4*>(k_cache + head + (size_t)j * HS + 8 * d8)
+                      : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float s[2];
+  float m = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int j = kw0 + lane + 64 * t;
+    float acc = 0.f;
+#pragma unroll
+    for (int d8 = 0; d8 < HS / 8; ++d8) {
+      const uint4 uq = *reinterpret_cast<const uint4*>(q + (size_t)b * C + h * HS + 8 * d8);
+      const unsigned wq[4] = {uq.x, uq.y, uq.z, uq.w};
+      const unsigned wd[4] = {kr[t][d8].x, kr[t][d8].y, kr[t][d8].z, kr[t][d8].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(bf2f(wq[e] & 0xffff), bf2f(wd[e] & 0xffff), acc);
+        acc = fmaf(bf2f(wq[e] >> 16), bf2f(wd[e] >> 16), acc);
+      }
+    }
+    s[t] = j <= pos ? acc * scale_log2 : -INFINITY;
+    m = fmaxf(m, s[t]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  // weights of keys past pos are 0 (also when the whole wave is past pos)
+  float l = 0.f;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float p = kw0 + lane + 64 * t <= pos ? __builtin_amdgcn_exp2f(s[t] - m) : 0.f;
+    ps[w][lane + 64 * t] = p;
+    l += p;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+  // the wave's weights are read back by other lanes of the same wave
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   float o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < KPG; ++u) {
-    const float pj = ps[kg * KPG + u];  // 0 beyond pos
+    const float pj = ps[w][kg * KPG + u];
     const unsigned wd[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -258,39 +307,58 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(const bf16_t* __restri
       o8[2 * e + 1] = fmaf(pj, bf2f(wd[e] >> 16), o8[2 * e + 1]);
     }
   }
+  // sum the key groups: lanes dg, dg + DG, ... hold the same columns
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ored[kg][8 * dg + e] = o8[e];
+  for (int o = DG; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o8[e] += __shfl_xor(o8[e], o);
+  if (kg == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wpart[w][2 + 8 * dg + e] = o8[e];
+  }
+  if (lane == 0) {
+    wpart[w][0] = m;
+    wpart[w][1] = l;
+  }
   __syncthreads();
+  // merge the waves (fixed order)
+  float mm = -INFINITY, ll = 0.f, oo = 0.f;
   if (tid < HS) {
-    float t = 0.f;
-    for (int g = 0; g < KG; ++g) t += ored[g][tid];
-    float* pr = part + ((size_t)bh * nchunk + chunk) * (HS + 2);
-    pr[2 + tid] = t;
-    if (tid == 0) {
-      pr[0] = m;
-      pr[1] = l;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) mm = fmaxf(mm, wpart[i][0]);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      const float a = wpart[i][1] > 0.f ? __builtin_amdgcn_exp2f(wpart[i][0] - mm) : 0.f;
+      ll = fmaf(wpart[i][1], a, ll);
+      oo = fmaf(wpart[i][2 + tid], a, oo);
     }
   }
-}
-
-// Merge the chunk partials of each (b, h): y_m[b][h*HS + d] = bf16(o / l)
-// with every chunk rescaled to the common maximum.
-template <int HS>
-__global__ __launch_bounds__(HS) void decode_combine_kernel(const float* __restrict__ part,
-                                                            bf16_t* __restrict__ ym, int H,
-                                                            int nchunk) {
-  const int bh = blockIdx.x, d = threadIdx.x;
-  const int b = bh / H, h = bh - b * H;
-  const float* pr = part + (size_t)bh * nchunk * (HS + 2);
-  float m = -INFINITY;
-  for (int c = 0; c < nchunk; ++c) m = fmaxf(m, pr[c * (HS + 2)]);
-  float l = 0.f, o = 0.f;
-  for (int c = 0; c < nchunk; ++c) {
-    const float a = __builtin_amdgcn_exp2f(pr[c * (HS + 2)] - m);
-    l = fmaf(pr[c * (HS + 2) + 1], a, l);
-    o = fmaf(pr[c * (HS + 2) + 2 + d], a, o);
+  if (nchunk == 1) {
+    if (tid < HS) ym[(size_t)b * C + h * HS + tid] = f2bf(oo / ll);
+    return;
   }
-  ym[(size_t)b * H * HS + h * HS + d] = f2bf(o / l);
+  if (tid < HS) {
+    float* pr = part + ((size_t)bh * nchunk + chunk) * (HS + 2);
+    st_dev(&pr[2 + tid], oo);
+    if (tid == 0) {
+      st_dev(&pr[0], mm);
+      st_dev(&pr[1], ll);
+    }
+  }
+  // the last chunk block of this (b, h) merges the chunks in order
+  if (!arrive_last(&counters[bh], (unsigned)nchunk, &is_last)) return;
+  if (tid < HS) {
+    const float* pr = part + (size_t)bh * nchunk * (HS + 2);
+    float cm = -INFINITY;
+    for (int c = 0; c < nchunk; ++c) cm = fmaxf(cm, ld_dev(&pr[c * (HS + 2)]));
+    float cl = 0.f, co = 0.f;
+    for (int c = 0; c < nchunk; ++c) {
+      const float a = __builtin_amdgcn_exp2f(ld_dev(&pr[c * (HS + 2)]) - cm);
+      cl = fmaf(ld_dev(&pr[c * (HS + 2) + 1]), a, cl);
+      co = fmaf(ld_dev(&pr[c * (HS + 2) + 2 + tid]), a, co);
+    }
+    ym[(size_t)b * C + h * HS + tid] = f2bf(co / cl);
+  }
 }
 
 // Copy the keys and values of positions [0, T) from the head-major q/k/v
@@ -311,7 +379,7 @@ __global__ void export_kv_kernel(const bf16_t* __restrict__ k, const bf16_t* __r
 
 // LDS bytes of one skinny-GEMM block.
 inline size_t skinny_lds_bytes(int B, int K) {
-  return (size_t)kDecWaves * B * kDecCols * sizeof(float) + (size_t)B * K * sizeof(bf16_t);
+  return (size_t)kDecWaves * 4 * B * 8 * sizeof(float) + (size_t)B * K * sizeof(bf16_t);
 }
 
 }  // namespace gpt_attn

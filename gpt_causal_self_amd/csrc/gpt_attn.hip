@@ -78,6 +78,14 @@ int gpt_attn_create(gpt_attn_t* out, int C, int n_head, int max_B, int max_T, in
   h->part_elems = L.part_elems;
   h->ln = h->ws + L.ln;
   h->rowstats = (float*)(h->ws + L.rowstats);
+  h->counters = (unsigned*)(h->ws + L.counters);
+  if (hipMemset(h->counters, 0, kCounters * sizeof(unsigned)) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(ws);
+    free(h);
+    return GPT_ATTN_ERR_HIP;
+  }
 
   *out = h;
   return GPT_ATTN_OK;

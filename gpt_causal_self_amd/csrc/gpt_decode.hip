@@ -8,6 +8,11 @@ using namespace gpt_attn;
 
 namespace {
 
+#ifndef GA_DEC_ATTN_THREADS
+#define GA_DEC_ATTN_THREADS 512
+#endif
+constexpr int kDecAttnThreads = GA_DEC_ATTN_THREADS;  // 128 cached keys per wave
+constexpr int kDecChunk = kDecAttnThreads / 64 * 128;
 inline int nchunks(int n) { return (n + kDecChunk - 1) / kDecChunk; }
 
 }  // namespace
@@ -26,8 +31,7 @@ int gpt_attn_decode(gpt_attn_t h, const void* x_new, int B, int pos, const void*
   const int C = h->C, H = h->H, hs = h->hs;
   if (skinny_lds_bytes(B, C) > 64 * 1024) return GPT_ATTN_ERR_UNSUPPORTED;
   const int nc = nchunks(pos + 1);
-  if ((size_t)B * H * nc * (hs + 2) > h->part_elems ||
-      (size_t)kDecKSplit * B * 3 * C > h->part_elems)
+  if ((size_t)B * H * nc * (hs + 2) > h->part_elems || B * H > kCounters)
     return GPT_ATTN_ERR_SHAPE;
   if (!aligned16(x_new) || !aligned16(W_attn) || !aligned16(W_proj) || !aligned16(k_cache) ||
       !aligned16(v_cache) || !aligned16(y) || (b_attn && !aligned16(b_attn)) ||
@@ -39,31 +43,27 @@ int gpt_attn_decode(gpt_attn_t h, const void* x_new, int B, int pos, const void*
   const hipStream_t st = as_stream(stream);
   bf16_t* q = (bf16_t*)h->qkv;  // [B][C]
   bf16_t* ym = (bf16_t*)h->o;   // [B][C]
-  float* part = h->part;        // [B*H][nc][hs + 2]
+  float* part = h->part;        // [B*H][nc][hs + 2] attention chunk partials
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hs));
+  // arrival counters of the attention's (b, h) blocks (used when the cache
+  // spans several chunks)
+  unsigned* cnt_attn = h->counters;
   DecQKVOut o1{q, (bf16_t*)k_cache, (bf16_t*)v_cache, C, H, hs, cache_T, pos};
-  hipLaunchKernelGGL(skinny_gemm_kernel, dim3((3 * C + kDecCols - 1) / kDecCols, kDecKSplit),
-                     dim3(64 * kDecWaves), skinny_lds_bytes(B, C), st, (const bf16_t*)x_new, B, C,
-                     (const bf16_t*)W_attn, 3 * C, part);
-  hipLaunchKernelGGL(skinny_finish_kernel<DecQKVOut>, dim3((B * 3 * C + 255) / 256), dim3(256),
-                     0, st, part, kDecKSplit, B, 3 * C, (const bf16_t*)b_attn, o1);
-  if (hs == 64) {
-    hipLaunchKernelGGL(decode_attn_kernel<64>, dim3(B * H, nc), dim3(256), 0, st, q,
-                       (const bf16_t*)k_cache, (const bf16_t*)v_cache, part, H, cache_T, pos, nc,
-                       scale_log2);
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3(B * H), dim3(64), 0, st, part, ym, H, nc);
-  } else {
-    hipLaunchKernelGGL(decode_attn_kernel<32>, dim3(B * H, nc), dim3(256), 0, st, q,
-                       (const bf16_t*)k_cache, (const bf16_t*)v_cache, part, H, cache_T, pos, nc,
-                       scale_log2);
-    hipLaunchKernelGGL(decode_combine_kernel<32>, dim3(B * H), dim3(32), 0, st, part, ym, H, nc);
-  }
+  hipLaunchKernelGGL(skinny_gemm_kernel<DecQKVOut>, dim3((3 * C + kDecCols - 1) / kDecCols),
+                     dim3(64 * kDecWaves), skinny_lds_bytes(B, C), st, (const bf16_t*)x_new, B,
+                     C, (const bf16_t*)W_attn, 3 * C, (const bf16_t*)b_attn, o1);
+  if (hs == 64)
+    hipLaunchKernelGGL((decode_attn_kernel<64, kDecAttnThreads>), dim3(B * H, nc), dim3(kDecAttnThreads), 0, st, q,
+                       (const bf16_t*)k_cache, (const bf16_t*)v_cache, part, ym, H, cache_T, pos,
+                       nc, scale_log2, cnt_attn);
+  else
+    hipLaunchKernelGGL((decode_attn_kernel<32, kDecAttnThreads>), dim3(B * H, nc), dim3(kDecAttnThreads), 0, st, q,
+                       (const bf16_t*)k_cache, (const bf16_t*)v_cache, part, ym, H, cache_T, pos,
+                       nc, scale_log2, cnt_attn);
   DecRowOut o2{(bf16_t*)y, C};
-  hipLaunchKernelGGL(skinny_gemm_kernel, dim3((C + kDecCols - 1) / kDecCols, kDecKSplit),
+  hipLaunchKernelGGL(skinny_gemm_kernel<DecRowOut>, dim3((C + kDecCols - 1) / kDecCols),
                      dim3(64 * kDecWaves), skinny_lds_bytes(B, C), st, ym, B, C,
-                     (const bf16_t*)W_proj, C, part);
-  hipLaunchKernelGGL(skinny_finish_kernel<DecRowOut>, dim3((B * C + 255) / 256), dim3(256), 0,
-                     st, part, kDecKSplit, B, C, (const bf16_t*)b_proj, o2);
+                     (const bf16_t*)W_proj, C, (const bf16_t*)b_proj, o2);
   return launch_status();
 }
 

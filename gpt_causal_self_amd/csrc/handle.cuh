@@ -54,6 +54,9 @@ struct gpt_attn_handle {
   void* ln;      // [B][T][C]     Pre-LN block: ln_1 of the input
   float* rowstats;  // backward: L (log2 units) and D per softmax row, rows of
                     // T rounded up to 64: [2][B][H][Tpad]
+  unsigned* counters;  // [kCounters] arrival counters of kernels whose last
+                       // block finishes the work of the others; zero between
+                       // launches (set at creation, reset by that last block)
   size_t part_elems;
   // state of the last forward
   int saved, saved_B, saved_T;
@@ -79,6 +82,7 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // number of row slices of the bias-gradient column sums.
 constexpr int kWgradSplits = 8;
 constexpr int kColsumSplits = 64;
+constexpr int kCounters = 4096;
 
 int check_dims(int C, int n_head, int max_B, int max_T, int dtype) {
   if (C <= 0 || n_head <= 0 || max_B <= 0 || max_T <= 0) return GPT_ATTN_ERR_INVALID_ARG;
@@ -92,7 +96,7 @@ int check_dims(int C, int n_head, int max_B, int max_T, int dtype) {
 }
 
 struct Layout {
-  size_t qkv, o, lse, dym, dqkv, delta, part, ln, rowstats, total, part_elems;
+  size_t qkv, o, lse, dym, dqkv, delta, part, ln, rowstats, counters, total, part_elems;
 };
 
 Layout layout(int C, int H, int max_B, int max_T, size_t es) {
@@ -110,6 +114,8 @@ Layout layout(int C, int H, int max_B, int max_T, size_t es) {
   L.ln = off;    off = align_up(off + BT * C * es);
   L.rowstats = off;
   off = align_up(off + 2 * (size_t)max_B * H * ((max_T + 63) / 64 * 64) * sizeof(float));
+  L.counters = off;
+  off = align_up(off + kCounters * sizeof(unsigned));
   L.total = off;
   return L;
 }

@@ -39,9 +39,11 @@ extern "C" {
  * workspace (a saved forward state is dropped).  B = 0 is a no-op.
  * Errors: INVALID_ARG (NULL pointer, B < 0, pos < 0, cache_T <= 0,
  * pos >= cache_T), SHAPE (n_head differs from the handle's, B > the handle's
- * max_B, or the per-chunk partials of B * n_head * ceil(cache_T / 256) rows
- * exceed the workspace), UNSUPPORTED (fp32 handle, B > 16, or B * C too
- * large for one block's LDS), ALIGN, HIP. */
+ * max_B, B * n_head > 4096, or the per-chunk partials of
+ * B * n_head * ceil((pos + 1) / 1024) rows exceed the workspace),
+ * UNSUPPORTED (fp32 handle, B > 16, or B * C too large for one block's LDS),
+ * ALIGN, HIP.  Calls that overlap on one handle race (they share its
+ * workspace and its arrival counters). */
 int gpt_attn_decode(gpt_attn_t h, const void *x_new, int B, int pos, const void *W_attn,
                     const void *b_attn, const void *W_proj, const void *b_proj, int n_head,
                     void *k_cache, void *v_cache, int cache_T, void *y, void *stream);

@@ -110,8 +110,8 @@ def test_prefill_then_decode():
 
 def test_decode_gpt2_124m_shape_across_chunk_boundaries():
     """GPT-2 124M attention shape (12 sequences, C=768, 12 heads): prefill
-    250 positions, then decode 250..265 (crossing the 256-key chunk of the
-    decode attention) and 508..520 after a second prefill."""
+    250 positions, then decode 250..265 and 508..520 after a second
+    prefill."""
     import torch
     B, T, C, H = 12, 521, 768, 12
     inp = _inputs(B, T, C, H, seed=77)
@@ -127,6 +127,27 @@ def test_decode_gpt2_124m_shape_across_chunk_boundaries():
         g = _decode_range(layer, d, H, kc, vc, t0, t1)
         _check_rows(g, inp, t0, t1)
     layer.close()
+
+
+@pytest.mark.parametrize("C,H", [(128, 4), (256, 4)])
+def test_decode_across_attention_blocks(C, H):
+    """Caches longer than one attention block (1024 keys): prefill 1021
+    positions, then decode 1021..1027, so that the keys of one query span one
+    and then two blocks whose partial results are merged (head sizes 32, 64)."""
+    import torch
+    B, T, T0 = 2, 1028, 1021
+    inp = _inputs(B, T, C, H, seed=31)
+    d = _dev(inp)
+    layer = ga.Layer(C, H, B, T, "bf16")
+    kc = torch.zeros((B, H, 1100, C // H), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    y0 = torch.empty((B, T0, C), dtype=torch.bfloat16, device="cuda")
+    ga.gpt_attn_forward(layer.h, d["x"][:, :T0].contiguous(), d["W_attn"], d["b_attn"],
+                        d["W_proj"], d["b_proj"], H, y0, B=B, T=T0)
+    ga.gpt_attn_export_kv(layer.h, kc, vc)
+    g = _decode_range(layer, d, H, kc, vc, T0, T)
+    layer.close()
+    _check_rows(g, inp, T0, T)
 
 
 def test_decode_is_deterministic():
