@@ -80,8 +80,20 @@ int gpt_attn_create(gpt_attn_t* out, int C, int n_head, int max_B, int max_T, in
   h->rowstats = (float*)(h->ws + L.rowstats);
   h->counters = (unsigned*)(h->ws + L.counters);
   if (hipMemset(h->counters, 0, kCounters * sizeof(unsigned)) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
+      hipDeviceSynchronize() != hipSuccess ||
+      hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess) {
     (void)hipGetLastError();
+    (void)hipFree(ws);
+    free(h);
+    return GPT_ATTN_ERR_HIP;
+  }
+  if (hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_mid, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
+    (void)hipGetLastError();
+    if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+    if (h->ev_mid) (void)hipEventDestroy(h->ev_mid);
+    (void)hipStreamDestroy(h->side);
     (void)hipFree(ws);
     free(h);
     return GPT_ATTN_ERR_HIP;
@@ -98,6 +110,10 @@ int gpt_attn_destroy(gpt_attn_t h) {
     if (hipDeviceSynchronize() != hipSuccess) rc = GPT_ATTN_ERR_HIP;
     if (hipFree(h->ws) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   }
+  if (h->ev_fork && hipEventDestroy(h->ev_fork) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
+  if (h->ev_mid && hipEventDestroy(h->ev_mid) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
+  if (h->ev_join && hipEventDestroy(h->ev_join) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
+  if (h->side && hipStreamDestroy(h->side) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   free(h);
   return rc;
 }
@@ -287,6 +303,10 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
                          0, st, (const bf16_t*)dY, (bf16_t*)h->ln, (long)M, C, dp);
       dY = h->ln;
     }
+    // Weight and bias gradients go to the handle's side stream, forked here
+    // (dY and o ready) and joined back into st at the end; the split-K and
+    // column-sum partials are used on the side stream only.
+    (void)hipEventRecord(h->ev_fork, st);
     // ---- c_proj: dym = dY W_proj^T (its epilogue also writes the softmax
     // backward row statistics D and L) ; dW_proj = ym^T dY ; db_proj = colsum(dY)
     const int Tpad = (T + 63) / 64 * 64;
@@ -301,16 +321,19 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
       launch_gemm2<GA_DGRAD_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M,
                                               C, C, e_dym, st);
     }
+    // the weight and bias gradients of c_proj need only dY and o: side stream
+    const hipStream_t sd = h->side;
+    (void)hipStreamWaitEvent(sd, h->ev_fork, 0);
     Epi2Partial e_wp{part, C, (size_t)C * C};
     const int s1 = splits_for(((C + 127) / 128) * ((C + 127) / 128));
     const int n1 = launch_gemm2<GA_WGRAD_TILE, false, false>(o, C, (const bf16_t*)dY, C, C, C, M,
-                                                             e_wp, st, s1);
-    hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, st, part, n1,
+                                                             e_wp, sd, s1);
+    hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, sd, part, n1,
                        (size_t)C * C, (size_t)C * C, (bf16_t*)dW_proj);
     if (db_proj) {
-      hipLaunchKernelGGL(colsum_bf16_kernel, dim3((C + 63) / 64, bcs), dim3(256), 0, st,
+      hipLaunchKernelGGL(colsum_bf16_kernel, dim3((C + 63) / 64, bcs), dim3(256), 0, sd,
                          (const bf16_t*)dY, M, C, C, brows, cpart);
-      hipLaunchKernelGGL(reduce_colparts_kernel<bf16_t>, dim3((C + 63) / 64), dim3(256), 0, st,
+      hipLaunchKernelGGL(reduce_colparts_kernel<bf16_t>, dim3((C + 63) / 64), dim3(256), 0, sd,
                          cpart, bcs, C, (bf16_t*)db_proj);
     }
     mark(h, 5, st);
@@ -349,21 +372,25 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     }
     mark(h, 6, st);
     // ---- c_attn: dx = dqkv W_attn^T ; dW_attn = x^T dqkv ; db_attn = colsum(dqkv)
-    Epi2RowMajor e_dx{(bf16_t*)dx, C, nullptr};
-    launch_gemm2<GA_DGRAD_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3, e_dx,
-                                            st);
+    (void)hipEventRecord(h->ev_mid, st);  // dqkv ready
+    (void)hipStreamWaitEvent(sd, h->ev_mid, 0);
     Epi2Partial e_wa{part, N3, (size_t)C * N3};
     const int s2 = splits_for(((C + 127) / 128) * ((N3 + 127) / 128));
     const int n2 = launch_gemm2<GA_WGRAD_TILE, false, false>((const bf16_t*)x, C, dqkv, N3, C, N3,
-                                                             M, e_wa, st, s2);
-    hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, st, part, n2,
+                                                             M, e_wa, sd, s2);
+    hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, sd, part, n2,
                        (size_t)C * N3, (size_t)C * N3, (bf16_t*)dW_attn);
     if (db_attn) {
-      hipLaunchKernelGGL(colsum_bf16_kernel, dim3((N3 + 63) / 64, bcs), dim3(256), 0, st, dqkv, M,
+      hipLaunchKernelGGL(colsum_bf16_kernel, dim3((N3 + 63) / 64, bcs), dim3(256), 0, sd, dqkv, M,
                          N3, N3, brows, cpart);
       hipLaunchKernelGGL(reduce_colparts_kernel<bf16_t>, dim3((N3 + 63) / 64), dim3(256), 0,
-                         st, cpart, bcs, N3, (bf16_t*)db_attn);
+                         sd, cpart, bcs, N3, (bf16_t*)db_attn);
     }
+    Epi2RowMajor e_dx{(bf16_t*)dx, C, nullptr};
+    launch_gemm2<GA_DGRAD_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3, e_dx,
+                                            st);
+    (void)hipEventRecord(h->ev_join, sd);
+    (void)hipStreamWaitEvent(st, h->ev_join, 0);
   } else {
     const float* qkv = (const float*)h->qkv;
     const float* o = (const float*)h->o;

@@ -71,6 +71,11 @@ struct gpt_attn_handle {
   // optional stage events (measurement hook)
   hipEvent_t ev[8];
   int n_ev;
+  // second stream of the backward (default priority, non-blocking): the
+  // weight and bias gradients run there beside the data-gradient chain,
+  // forked from and joined back into the caller's stream by these events
+  hipStream_t side;
+  hipEvent_t ev_fork, ev_mid, ev_join;
 };
 
 namespace {

@@ -33,6 +33,20 @@ __global__ __launch_bounds__(256) void layernorm_bf16_kernel(const bf16_t* __res
   if (row >= M) return;
   const int nch = C >> 3;
   const bf16_t* xr = x + (size_t)row * C;
+  // weight and bias chunks: they do not depend on the statistics, so rows of
+  // up to 256 chunks load them first (longer rows load them at the end, to
+  // keep the registers for the row itself)
+  constexpr bool kEarly = CH <= 4;
+  auto load_wb = [&](int k, uint4& wk, uint4& bk) {
+    const int c = lane + 64 * k;
+    wk = c < nch ? *reinterpret_cast<const uint4*>(w + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    bk = (b && c < nch) ? *reinterpret_cast<const uint4*>(b + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+  };
+  uint4 wv[kEarly ? CH : 1], bv[kEarly ? CH : 1];
+  if constexpr (kEarly) {
+#pragma unroll
+    for (int k = 0; k < CH; ++k) load_wb(k, wv[k], bv[k]);
+  }
   float v[CH][8];
   float s = 0.f;
 #pragma unroll
@@ -71,13 +85,15 @@ __global__ __launch_bounds__(256) void layernorm_bf16_kernel(const bf16_t* __res
   for (int k = 0; k < CH; ++k) {
     const int c = lane + 64 * k;
     if (c < nch) {
-      const uint4 uw = *reinterpret_cast<const uint4*>(w + 8 * c);
-      const unsigned ww[4] = {uw.x, uw.y, uw.z, uw.w};
-      unsigned bb[4] = {0u, 0u, 0u, 0u};
-      if (b) {
-        const uint4 ub = *reinterpret_cast<const uint4*>(b + 8 * c);
-        bb[0] = ub.x; bb[1] = ub.y; bb[2] = ub.z; bb[3] = ub.w;
+      uint4 wk, bk;
+      if constexpr (kEarly) {
+        wk = wv[k];
+        bk = bv[k];
+      } else {
+        load_wb(k, wk, bk);
       }
+      const unsigned ww[4] = {wk.x, wk.y, wk.z, wk.w};
+      const unsigned bb[4] = {bk.x, bk.y, bk.z, bk.w};
       unsigned o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
