@@ -255,9 +255,23 @@ struct Epi2QKV {
 };
 
 // Exact GELU, g(v) = v * Phi(v) = v/2 * (1 + erf(v / sqrt(2))) (page "nanoGPT
-// architecture explained step by step", section 4).
+// architecture explained step by step", section 4), with erf from Abramowitz
+// and Stegun, Handbook of Mathematical Functions, formula 7.1.26: for a >= 0,
+// erfc(a) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2) + e(a),
+// t = 1 / (1 + p a), |e(a)| <= 1.5e-7.  With a = |v| / sqrt(2),
+// g(v) = v - v/2 erfc(a) for v >= 0 and v/2 erfc(a) for v < 0, so the negative
+// tail is a product (no cancellation in 1 + erf); |g - exact| <= |v| 7.5e-8
+// before rounding, far below the bf16 step of the stored activation.
 __device__ __forceinline__ float gelu_erf(float v) {
-  return 0.5f * v * (1.f + erff(v * 0.70710678118654752f));
+  const float a = fabsf(v) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.f));
+  float q = fmaf(1.061405429f, t, -1.453152027f);
+  q = fmaf(q, t, 1.421413741f);
+  q = fmaf(q, t, -0.284496736f);
+  q = fmaf(q, t, 0.254829592f);
+  const float erfc = q * t * __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
+  const float h = 0.5f * v * erfc;
+  return v >= 0.f ? v - h : h;
 }
 
 // MLP c_fc epilogue: bias, exact GELU, rounding; row-major [M][ldc].
