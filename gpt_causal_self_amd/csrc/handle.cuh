@@ -33,7 +33,7 @@
 #define GA_FC_TILE 192, 384, 2, 64, 2, 4, true, false, 1
 #endif
 #ifndef GA_FCPROJ_TILE
-#define GA_FCPROJ_TILE 128, 128, 3, 32, 2, 2, true, false, 3
+#define GA_FCPROJ_TILE 192, 256, 2, 64, 2, 4, true, false, 1
 #endif
 
 
