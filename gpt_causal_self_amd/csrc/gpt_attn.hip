@@ -375,9 +375,14 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     (void)hipEventRecord(h->ev_mid, st);  // dqkv ready
     (void)hipStreamWaitEvent(sd, h->ev_mid, 0);
     Epi2Partial e_wa{part, N3, (size_t)C * N3};
-    const int s2 = splits_for(((C + 127) / 128) * ((N3 + 127) / 128));
-    const int n2 = launch_gemm2<GA_WGRAD_TILE, false, false>((const bf16_t*)x, C, dqkv, N3, C, N3,
-                                                             M, e_wa, sd, s2);
+    int s2;
+    {
+      constexpr int tile[] = {GA_WGRAD_ATTN_TILE};
+      const int tiles = ((C + tile[0] - 1) / tile[0]) * ((N3 + tile[1] - 1) / tile[1]);
+      s2 = std::max(1, std::min(kWgradSplits, 256 * GA_WGRAD_ATTN_PER_CU / tiles));
+    }
+    const int n2 = launch_gemm2<GA_WGRAD_ATTN_TILE, false, false>(
+        (const bf16_t*)x, C, dqkv, N3, C, N3, M, e_wa, sd, s2);
     hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, sd, part, n2,
                        (size_t)C * N3, (size_t)C * N3, (bf16_t*)dW_attn);
     if (db_attn) {

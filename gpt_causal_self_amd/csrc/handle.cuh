@@ -27,6 +27,13 @@
 #ifndef GA_WGRAD_TILE
 #define GA_WGRAD_TILE 128, 128, 2, 64, 2, 2
 #endif
+// weight gradient of c_attn (C x 3C over all B*T rows): large tiles, one per CU
+#ifndef GA_WGRAD_ATTN_TILE
+#define GA_WGRAD_ATTN_TILE 256, 256, 2, 64, 2, 4
+#endif
+#ifndef GA_WGRAD_ATTN_PER_CU
+#define GA_WGRAD_ATTN_PER_CU 1
+#endif
 // MLP: c_fc [C -> 4C] with the GELU epilogue, c_proj [4C -> C] (waves per
 // SIMD as the last value).
 #ifndef GA_FC_TILE
