@@ -10,11 +10,12 @@
 // values of positions 0..pos-1 from a cache: this file computes that step.
 //
 //   skinny_gemm_kernel   out[b][n] = sum_c x[b][c] W[c][n] (+ bias) for a
-//                        handful of rows b (the batch); HBM-bound on W.  A
-//                        block takes 16 columns over all rows c and applies
-//                        the epilogue itself, which either scatters q / k / v
-//                        (q to a buffer, k and v into the caches at `pos`) or
-//                        writes a row-major output.
+//                        handful of rows b (the batch, <= 16); HBM-bound on
+//                        W.  A block takes 16 columns over all rows c on the
+//                        matrix cores and applies the epilogue itself, which
+//                        either scatters q / k / v (q to a buffer, k and v
+//                        into the caches at `pos`) or writes a row-major
+//                        output.
 //   decode_attn_kernel   per (b, h) and chunk of 128 cached keys per wave:
 //                        scores, max, exp2 weights, sum and the weighted
 //                        value sum; HBM-bound on the cache.  With one chunk
@@ -98,117 +99,95 @@ struct DecRowOut {
   }
 };
 
-// out.put(b, n, sum_c x[b][c] W[c][n] + bias[n]) for b < B (<= kDecMaxB) and
-// the block's kDecCols = 16 columns n.  512 threads = 8 waves; in a wave lane
-// = ks + 32 * cg: cg picks 8 consecutive columns (one 16-byte load per row)
-// and the row slot r = 32 * w + ks takes the rows c = r, r + 256, ...; up to
-// kDecUnroll of a lane's rows are loaded at once, the first batch before x
-// is staged in LDS (bf16), so that the two loads overlap.  Sums are reduced
-// over the 16 row slots of a 16-lane row with DPP moves and then over the
-// 16 rows of a column group (2 per wave) from LDS, in a fixed order: the
-// result is deterministic.
-#ifndef GA_DEC_WAVES
-#define GA_DEC_WAVES 8
-#endif
-constexpr int kDecWaves = GA_DEC_WAVES;
-constexpr int kDecRowSlots = 32 * kDecWaves;  // rows in flight per pass
-constexpr int kDecUnroll = 8;                 // passes loaded together
+// out.put(b, n, sum_c x[b][c] W[c][n] + bias[n]) for b < B (<= kDecMaxB = 16)
+// and the block's kDecCols = 16 columns n, on the matrix cores:
+// v_mfma_f32_16x16x32_bf16 with A = the W slice transposed (16 columns n x 32
+// rows c) and B = x transposed (32 rows c x 16 batch rows b), so that
+// D[i][j] = out[j][n0 + i] and the sum over c runs inside the MFMA.  The rows
+// go in k-steps of 32; wave w takes the steps w, w + 8, ..., kDecBatchSteps
+// at a time, and copies the W rows of those steps (32 B per row: 16 columns)
+// into its own LDS slots with global_load_lds_dwordx4 (one 1 KB load per
+// step), so it needs no barrier before reading them: lane l of 16-lane group G = l / 16 reads, with
+// ds_read_b64_tr_b16, rows 8G + 4t + (l % 16) / 4 (t = 0, 1) at column
+// 4 (l % 4) of the step, which hands it the A operand (column l % 16, rows
+// 8G .. 8G + 7).  Its B operand, x[b][8G .. 8G + 7] with b = l % 16, is one
+// 16-byte load.  The 8 waves' 16 x 16 accumulators are summed in LDS (fixed
+// order: deterministic) and the epilogue applied.
+constexpr int kDecWaves = 8;
+constexpr int kDecBatchSteps = 4;   // k-steps whose x operands are loaded together
+
+__device__ __align__(16) static const uint4 g_dec_zero16 = {0u, 0u, 0u, 0u};
 
 template <class Out>
 __global__ __launch_bounds__(64 * kDecWaves) void skinny_gemm_kernel(
     const bf16_t* __restrict__ x, int B, int K, const bf16_t* __restrict__ W, int N,
     const bf16_t* __restrict__ bias, Out out) {
-  extern __shared__ float dsm[];
-  float* red = dsm;                                         // [kDecWaves * 4][B][8]
-  bf16_t* xs = reinterpret_cast<bf16_t*>(dsm + kDecWaves * 4 * B * 8);  // [B][K], 16-B aligned
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int ks = lane & 31, cg = lane >> 5;
-  const int n = blockIdx.x * kDecCols + 8 * cg;
-  const int r0 = 32 * w + ks;
-  constexpr int kStep = kDecRowSlots * kDecUnroll;
-  auto load_rows = [&](int cb, uint4 (&u)[kDecUnroll]) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef short v8i16 __attribute__((ext_vector_type(8)));
+  extern __shared__ __align__(16) char dsm[];
+  float* red = reinterpret_cast<float*>(dsm);                     // [kDecWaves][64][4]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // this wave's W slots: kDecBatchSteps k-steps of [32 rows][32 B]
+  char* wslot = dsm + kDecWaves * 64 * 4 * sizeof(float) + w * kDecBatchSteps * 1024;
+  const int n0 = blockIdx.x * kDecCols;
+  const int nsteps = (K + 31) / 32;
+  const int bj = lane & 15, g = lane >> 4;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int st0 = w; st0 < nsteps; st0 += kDecWaves * kDecBatchSteps) {
+    // W rows of this batch's steps -> the wave's slots (lane -> row lane / 2,
+    // 8 columns at 8 (lane % 2)), and the x operands
 #pragma unroll
-    for (int q = 0; q < kDecUnroll; ++q) {
-      const int c = cb + q * kDecRowSlots;
-      u[q] = (n < N && c < K) ? *reinterpret_cast<const uint4*>(W + (size_t)c * N + n)
-                              : make_uint4(0u, 0u, 0u, 0u);
+    for (int q = 0; q < kDecBatchSteps; ++q) {
+      const int st = st0 + q * kDecWaves;
+      if (st < nsteps) {
+        const int row = st * 32 + (lane >> 1);
+        const bf16_t* src = row < K ? W + (size_t)row * N + n0 + 8 * (lane & 1)
+                                    : reinterpret_cast<const bf16_t*>(&g_dec_zero16);
+        __builtin_amdgcn_load_to_lds(
+            (void*)src, (__attribute__((address_space(3))) void*)(wslot + q * 1024), 16, 0, 0);
+      }
     }
-  };
-  uint4 u[kDecUnroll];
-  load_rows(r0, u);
-  for (int i = tid; i < B * K / 8; i += 64 * kDecWaves)  // K % 8 == 0: 16-byte chunks
-    reinterpret_cast<uint4*>(xs)[i] = reinterpret_cast<const uint4*>(x)[i];
+    bf16x8 xf[kDecBatchSteps];
+#pragma unroll
+    for (int q = 0; q < kDecBatchSteps; ++q) {
+      const int st = st0 + q * kDecWaves, k = st * 32 + 8 * g;
+      xf[q] = (st < nsteps && bj < B && k < K)
+                  ? *reinterpret_cast<const bf16x8*>(x + (size_t)bj * K + k)
+                  : bf16x8{};
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads have landed
+#pragma unroll
+    for (int q = 0; q < kDecBatchSteps; ++q) {
+      const int st = st0 + q * kDecWaves;
+      if (st >= nsteps) break;
+      v4i16 r[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        r[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4i16*)(wslot + q * 1024 +
+                                                       (8 * g + 4 * t + (bj >> 2)) * 32 +
+                                                       (bj & 3) * 8));
+      const v8i16 av = {r[0][0], r[0][1], r[0][2], r[0][3], r[1][0], r[1][1], r[1][2], r[1][3]};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), xf[q], acc,
+                                                    0, 0, 0);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slots read before the next batch
+  }
+  // lane l holds D[4 (l / 16) + r][l % 16], r = 0..3
+  *reinterpret_cast<floatx4*>(red + (w * 64 + lane) * 4) = acc;
   __syncthreads();
-  float acc[kDecMaxB][8];
-#pragma unroll
-  for (int b = 0; b < kDecMaxB; ++b)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[b][e] = 0.f;
-  auto fma_rows = [&](int cb, const uint4 (&uu)[kDecUnroll]) {
-#pragma unroll
-    for (int q = 0; q < kDecUnroll; ++q) {
-      const int c = cb + q * kDecRowSlots;
-      if (c >= K) break;
-      const unsigned wd[4] = {uu[q].x, uu[q].y, uu[q].z, uu[q].w};
-      float wf[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        wf[2 * e] = bf2f(wd[e] & 0xffff);
-        wf[2 * e + 1] = bf2f(wd[e] >> 16);
-      }
-#pragma unroll
-      for (int b = 0; b < kDecMaxB; ++b) {
-        if (b < B) {
-          const float xv = bf2f(xs[b * K + c]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[b][e] = fmaf(xv, wf[e], acc[b][e]);
-        }
-      }
-    }
-  };
-  fma_rows(r0, u);
-  for (int cb = r0 + kStep; cb < K; cb += kStep) {
-    load_rows(cb, u);
-    fma_rows(cb, u);
-  }
-  // sum over the 16 lanes of a DPP row: swap neighbours, swap pairs, mirror
-  // the half-row, mirror the row; every lane of the row then holds its total
-#pragma unroll
-  for (int b = 0; b < kDecMaxB; ++b) {
-    if (b < B) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[b][e];
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-        acc[b][e] = v;
-      }
-    }
-  }
-  // rows 0, 1 of the wave hold column group 0, rows 2, 3 group 1
-  if ((lane & 15) == 0) {
-    const int row = w * 4 + (lane >> 4);
-#pragma unroll
-    for (int b = 0; b < kDecMaxB; ++b)  // unrolled: acc stays in registers
-      if (b < B)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[((size_t)row * B + b) * 8 + e] = acc[b][e];
-  }
-  __syncthreads();
-  for (int i = tid; i < B * kDecCols; i += 64 * kDecWaves) {
-    const int b = i / kDecCols, col = i - b * kDecCols;
-    const int nn = blockIdx.x * kDecCols + col;
-    if (nn >= N) continue;
-    const int g = col >> 3, e = col & 7;
+  const int o = threadIdx.x;  // output (i, j) = (o / 16, o % 16)
+  if (o < 256) {
+    const int i = o >> 4, j = o & 15;
+    const int l = (i >> 2) * 16 + j, r = i & 3;
     float v = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) v += red[((size_t)(ww * 4 + 2 * g + h) * B + b) * 8 + e];
-    if (bias) v += bf2f(bias[nn]);
-    out.put(b, nn, v);
+    for (int ww = 0; ww < kDecWaves; ++ww) v += red[(ww * 64 + l) * 4 + r];
+    const int n = n0 + i;
+    if (j < B && n < N) {
+      if (bias) v += bf2f(bias[n]);
+      out.put(j, n, v);
+    }
   }
 }
 
@@ -378,8 +357,8 @@ __global__ void export_kv_kernel(const bf16_t* __restrict__ k, const bf16_t* __r
 }
 
 // LDS bytes of one skinny-GEMM block.
-inline size_t skinny_lds_bytes(int B, int K) {
-  return (size_t)kDecWaves * 4 * B * 8 * sizeof(float) + (size_t)B * K * sizeof(bf16_t);
+inline size_t skinny_lds_bytes() {
+  return (size_t)kDecWaves * 64 * 4 * sizeof(float) + (size_t)kDecWaves * kDecBatchSteps * 1024;
 }
 
 }  // namespace gpt_attn

@@ -29,7 +29,6 @@ int gpt_attn_decode(gpt_attn_t h, const void* x_new, int B, int pos, const void*
   if (n_head != h->H || B > h->max_B) return GPT_ATTN_ERR_SHAPE;
   if (B > kDecMaxB) return GPT_ATTN_ERR_UNSUPPORTED;
   const int C = h->C, H = h->H, hs = h->hs;
-  if (skinny_lds_bytes(B, C) > 64 * 1024) return GPT_ATTN_ERR_UNSUPPORTED;
   const int nc = nchunks(pos + 1);
   if ((size_t)B * H * nc * (hs + 2) > h->part_elems || B * H > kCounters)
     return GPT_ATTN_ERR_SHAPE;
@@ -50,7 +49,7 @@ int gpt_attn_decode(gpt_attn_t h, const void* x_new, int B, int pos, const void*
   unsigned* cnt_attn = h->counters;
   DecQKVOut o1{q, (bf16_t*)k_cache, (bf16_t*)v_cache, C, H, hs, cache_T, pos};
   hipLaunchKernelGGL(skinny_gemm_kernel<DecQKVOut>, dim3((3 * C + kDecCols - 1) / kDecCols),
-                     dim3(64 * kDecWaves), skinny_lds_bytes(B, C), st, (const bf16_t*)x_new, B,
+                     dim3(64 * kDecWaves), skinny_lds_bytes(), st, (const bf16_t*)x_new, B,
                      C, (const bf16_t*)W_attn, 3 * C, (const bf16_t*)b_attn, o1);
   if (hs == 64)
     hipLaunchKernelGGL((decode_attn_kernel<64, kDecAttnThreads>), dim3(B * H, nc), dim3(kDecAttnThreads), 0, st, q,
@@ -62,7 +61,7 @@ int gpt_attn_decode(gpt_attn_t h, const void* x_new, int B, int pos, const void*
                        nc, scale_log2, cnt_attn);
   DecRowOut o2{(bf16_t*)y, C};
   hipLaunchKernelGGL(skinny_gemm_kernel<DecRowOut>, dim3((C + kDecCols - 1) / kDecCols),
-                     dim3(64 * kDecWaves), skinny_lds_bytes(B, C), st, ym, B, C,
+                     dim3(64 * kDecWaves), skinny_lds_bytes(), st, ym, B, C,
                      (const bf16_t*)W_proj, C, (const bf16_t*)b_proj, o2);
   return launch_status();
 }

@@ -41,7 +41,7 @@ extern "C" {
  * pos >= cache_T), SHAPE (n_head differs from the handle's, B > the handle's
  * max_B, B * n_head > 4096, or the per-chunk partials of
  * B * n_head * ceil((pos + 1) / 1024) rows exceed the workspace),
- * UNSUPPORTED (fp32 handle, B > 16, or B * C too large for one block's LDS),
+ * UNSUPPORTED (fp32 handle or B > 16),
  * ALIGN, HIP.  Calls that overlap on one handle race (they share its
  * workspace and its arrival counters). */
 int gpt_attn_decode(gpt_attn_t h, const void *x_new, int B, int pos, const void *W_attn,
