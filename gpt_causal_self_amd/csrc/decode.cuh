@@ -35,11 +35,11 @@
 #pragma once
 
 #include "common.cuh"
+#include "skinny.cuh"
 
 namespace gpt_attn {
 
 constexpr int kDecMaxB = 16;     // rows of one decode call
-constexpr int kDecCols = 16;     // output columns per skinny-GEMM block
 
 // Device-scope accesses of the fp32 partials that one block writes and the
 // last block of its group reads back.  Relaxed atomics at agent scope are
@@ -100,94 +100,21 @@ struct DecRowOut {
 };
 
 // out.put(b, n, sum_c x[b][c] W[c][n] + bias[n]) for b < B (<= kDecMaxB = 16)
-// and the block's kDecCols = 16 columns n, on the matrix cores:
-// v_mfma_f32_16x16x32_bf16 with A = the W slice transposed (16 columns n x 32
-// rows c) and B = x transposed (32 rows c x 16 batch rows b), so that
-// D[i][j] = out[j][n0 + i] and the sum over c runs inside the MFMA.  The rows
-// go in k-steps of 32; wave w takes the steps w, w + 8, ..., kDecBatchSteps
-// at a time, and copies the W rows of those steps (32 B per row: 16 columns)
-// into its own LDS slots with global_load_lds_dwordx4 (one 1 KB load per
-// step), so it needs no barrier before reading them: lane l of 16-lane group G = l / 16 reads, with
-// ds_read_b64_tr_b16, rows 8G + 4t + (l % 16) / 4 (t = 0, 1) at column
-// 4 (l % 4) of the step, which hands it the A operand (column l % 16, rows
-// 8G .. 8G + 7).  Its B operand, x[b][8G .. 8G + 7] with b = l % 16, is one
-// 16-byte load.  The 8 waves' 16 x 16 accumulators are summed in LDS (fixed
-// order: deterministic) and the epilogue applied.
-constexpr int kDecWaves = 8;
-constexpr int kDecBatchSteps = 4;   // k-steps whose x operands are loaded together
-
-__device__ __align__(16) static const uint4 g_dec_zero16 = {0u, 0u, 0u, 0u};
-
+// and the block's kDecCols = 16 columns n (skinny.cuh: the MFMA block).
 template <class Out>
 __global__ __launch_bounds__(64 * kDecWaves) void skinny_gemm_kernel(
     const bf16_t* __restrict__ x, int B, int K, const bf16_t* __restrict__ W, int N,
     const bf16_t* __restrict__ bias, Out out) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  typedef short v8i16 __attribute__((ext_vector_type(8)));
   extern __shared__ __align__(16) char dsm[];
-  float* red = reinterpret_cast<float*>(dsm);                     // [kDecWaves][64][4]
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // this wave's W slots: kDecBatchSteps k-steps of [32 rows][32 B]
-  char* wslot = dsm + kDecWaves * 64 * 4 * sizeof(float) + w * kDecBatchSteps * 1024;
   const int n0 = blockIdx.x * kDecCols;
-  const int nsteps = (K + 31) / 32;
-  const int bj = lane & 15, g = lane >> 4;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int st0 = w; st0 < nsteps; st0 += kDecWaves * kDecBatchSteps) {
-    // W rows of this batch's steps -> the wave's slots (lane -> row lane / 2,
-    // 8 columns at 8 (lane % 2)), and the x operands
-#pragma unroll
-    for (int q = 0; q < kDecBatchSteps; ++q) {
-      const int st = st0 + q * kDecWaves;
-      if (st < nsteps) {
-        const int row = st * 32 + (lane >> 1);
-        const bf16_t* src = row < K ? W + (size_t)row * N + n0 + 8 * (lane & 1)
-                                    : reinterpret_cast<const bf16_t*>(&g_dec_zero16);
-        __builtin_amdgcn_load_to_lds(
-            (void*)src, (__attribute__((address_space(3))) void*)(wslot + q * 1024), 16, 0, 0);
-      }
-    }
-    bf16x8 xf[kDecBatchSteps];
-#pragma unroll
-    for (int q = 0; q < kDecBatchSteps; ++q) {
-      const int st = st0 + q * kDecWaves, k = st * 32 + 8 * g;
-      xf[q] = (st < nsteps && bj < B && k < K)
-                  ? *reinterpret_cast<const bf16x8*>(x + (size_t)bj * K + k)
-                  : bf16x8{};
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's loads have landed
-#pragma unroll
-    for (int q = 0; q < kDecBatchSteps; ++q) {
-      const int st = st0 + q * kDecWaves;
-      if (st >= nsteps) break;
-      v4i16 r[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        r[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4i16*)(wslot + q * 1024 +
-                                                       (8 * g + 4 * t + (bj >> 2)) * 32 +
-                                                       (bj & 3) * 8));
-      const v8i16 av = {r[0][0], r[0][1], r[0][2], r[0][3], r[1][0], r[1][1], r[1][2], r[1][3]};
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), xf[q], acc,
-                                                    0, 0, 0);
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // slots read before the next batch
-  }
-  // lane l holds D[4 (l / 16) + r][l % 16], r = 0..3
-  *reinterpret_cast<floatx4*>(red + (w * 64 + lane) * 4) = acc;
-  __syncthreads();
+  skinny_mfma(x, K, B, K, W, N, n0, dsm);
+  const float* red = reinterpret_cast<const float*>(dsm);
   const int o = threadIdx.x;  // output (i, j) = (o / 16, o % 16)
   if (o < 256) {
     const int i = o >> 4, j = o & 15;
-    const int l = (i >> 2) * 16 + j, r = i & 3;
-    float v = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) v += red[(ww * 64 + l) * 4 + r];
+    const float v = red[((i >> 2) * 16 + j) * 4 + (i & 3)];
     const int n = n0 + i;
-    if (j < B && n < N) {
-      if (bias) v += bf2f(bias[n]);
-      out.put(j, n, v);
-    }
+    if (j < B && n < N) out.put(j, n, bias ? v + bf2f(bias[n]) : v);
   }
 }
 
@@ -356,9 +283,5 @@ __global__ void export_kv_kernel(const bf16_t* __restrict__ k, const bf16_t* __r
   }
 }
 
-// LDS bytes of one skinny-GEMM block.
-inline size_t skinny_lds_bytes() {
-  return (size_t)kDecWaves * 64 * 4 * sizeof(float) + (size_t)kDecWaves * kDecBatchSteps * 1024;
-}
 
 }  // namespace gpt_attn

@@ -6,6 +6,7 @@
 
 #include "attn_fwd.cuh"
 #include "gemm2.cuh"
+#include "skinny.cuh"
 #include "handle.cuh"
 
 namespace gpt_attn {
@@ -94,6 +95,40 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(const float* __restr
     epi(m, n, v);
 }
 
+// A projection of at most a few dozen rows (a short sequence) on the matrix
+// cores: the decode path's skinny block (16 columns over all K per block,
+// the sum over K inside v_mfma_f32_16x16x32_bf16) over 16-row chunks
+// (gridDim.y), each thread handing 4 consecutive columns of one row to the
+// projection's own epilogue (bias, q/k/v scatter, residual, dropout).  A is
+// k-contiguous [M][lda], B row-contiguous [K][ldb = N].
+#ifndef GA_SKINNY_MAX_M
+#define GA_SKINNY_MAX_M 16
+#endif
+template <class Epi>
+__global__ __launch_bounds__(64 * kDecWaves) void skinny_epi_kernel(const bf16_t* __restrict__ A,
+                                                                    int lda, int M, int K,
+                                                                    const bf16_t* __restrict__ Bm,
+                                                                    int N, Epi epi) {
+  extern __shared__ __align__(16) char dsm[];
+  const int n0 = blockIdx.x * kDecCols, m0 = blockIdx.y * 16;
+  skinny_mfma(A + (size_t)m0 * lda, lda, min(16, M - m0), K, Bm, N, n0, dsm);
+  const float* red = reinterpret_cast<const float*>(dsm);
+  const int o = threadIdx.x;  // row j = o % 16, columns n0 + 4 (o / 16) + 0..3
+  if (o < 64) {
+    const int j = o & 15, q = o >> 4;
+    const int m = m0 + j, n = n0 + 4 * q;
+    if (m < M && n < N) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = red[(q * 16 + j) * 4 + r];
+      if constexpr (SplitOffsets<Epi>::value)
+        epi.store(epi.row_off(m) + epi.col_off(n), n, v);
+      else
+        epi(m, n, v);
+    }
+  }
+}
+
 // The projection GEMM, split along K when it has fewer than 128 output
 // tiles: up to 8 slices (each at least 2 k-tiles), as many as give about
 // 256 blocks and fit the partial buffer.
@@ -101,6 +136,13 @@ template <int BM, int BN, int NSTAGE, int BK, int WGM, int WGN, bool A_KC, bool 
           int OCC = 1, class Epi>
 inline void launch_proj(const gpt_attn_handle* h, const bf16_t* A, int lda, const bf16_t* Bm,
                         int ldb, int M, int N, int K, const Epi& epi, hipStream_t st) {
+  if constexpr (A_KC && !B_KC) {
+    if (M <= GA_SKINNY_MAX_M && N % kDecCols == 0 && K % 8 == 0 && ldb == N) {
+      hipLaunchKernelGGL(skinny_epi_kernel<Epi>, dim3(N / kDecCols, (M + 15) / 16),
+                         dim3(64 * kDecWaves), skinny_lds_bytes(), st, A, lda, M, K, Bm, N, epi);
+      return;
+    }
+  }
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int nk = (K + BK - 1) / BK;
   int s = tiles >= 128 ? 1 : std::min(std::min(256 / std::max(tiles, 1), nk / 2), 8);
