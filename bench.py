@@ -137,14 +137,23 @@ def sources_digest():
     return h.hexdigest()
 
 
+def newest_counter_file(run_dir):
+    """The counter file of the latest rocprofv3 run under run_dir (each run
+    writes one <pid>_counter_collection.csv; a directory that collected
+    several runs must not mix them: dispatch ids repeat across runs)."""
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    return [max(files, key=os.path.getmtime)]
+
+
 def _counter_means(run_dir, counter):
     """Mean per-dispatch value of one counter, per kernel group and for the
     calibration copy, from a rocprofv3 -f csv output directory."""
     import csv
     import glob
-    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    files = newest_counter_file(run_dir)
     sums, counts = {}, {}
     for f in files:
         for r in csv.DictReader(open(f)):
@@ -228,9 +237,7 @@ def write_util(run_dir):
     import csv
     import glob
     import re
-    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
-    if not files:
-        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    files = newest_counter_file(run_dir)
     per = {}   # kernel -> dispatch -> counter -> [sum, max]
     for f in files:
         for r in csv.DictReader(open(f)):
