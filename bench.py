@@ -769,6 +769,9 @@ def main():
         cb = cpu_baseline(2, args.cpu_seqs)
         out["cpu_baseline"] = {k: (round(v, 6) if isinstance(v, float) else v)
                                for k, v in cb.items()}
+        if cb.get("value"):
+            # the same workload's rate on the GPU over the oracle's on the host
+            out["cpu_baseline"]["gpu_over_cpu"] = round(out["value"] / cb["value"], 1)
     layer.close()
     print(json.dumps(out))
 
