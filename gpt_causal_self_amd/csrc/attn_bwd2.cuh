@@ -49,11 +49,26 @@ struct Epi2DgradRowStats {
   static constexpr bool kStaged = true;
   static constexpr bool kStore8All = true;
   __device__ __forceinline__ const bf16_t* bias_ptr() const { return bias; }
-  __device__ __forceinline__ void store8_all(int m, int n, uint4 w, bool ok, int lane) const {
+  // O's chunk and the row's log-sum-exp, loaded ahead of the stores
+  struct Extra {
+    uint4 o;
+    float lse;
+  };
+  __device__ __forceinline__ Extra extra(int m, int n, bool ok) const {
+    Extra e{make_uint4(0u, 0u, 0u, 0u), 0.f};
+    if (ok) {
+      e.o = *reinterpret_cast<const uint4*>(O + (size_t)m * ldc + n);
+      const int b = m / T, t = m - b * T, h = n / HS;
+      e.lse = lse[((size_t)b * H + h) * T + t];
+    }
+    return e;
+  }
+  __device__ __forceinline__ void store8_all(int m, int n, uint4 w, bool ok, int lane,
+                                             const Extra& ex) const {
     float s = 0.f;
     if (ok) {
       *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = w;
-      const uint4 o = *reinterpret_cast<const uint4*>(O + (size_t)m * ldc + n);
+      const uint4 o = ex.o;
       const unsigned wa[4] = {w.x, w.y, w.z, w.w}, wo[4] = {o.x, o.y, o.z, o.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -66,7 +81,7 @@ struct Epi2DgradRowStats {
       const int b = m / T, t = m - b * T, h = n / HS;
       const size_t bh = (size_t)b * H + h;
       Dpad[bh * Tpad + t] = s;
-      Lpad[bh * Tpad + t] = lse[bh * T + t] * kLog2eB;
+      Lpad[bh * Tpad + t] = ex.lse * kLog2eB;
     }
   }
 };

@@ -312,9 +312,10 @@ struct Staged { static constexpr bool value = false; };
 template <class Epi>
 struct Staged<Epi, decltype(void(Epi::kStaged))> { static constexpr bool value = Epi::kStaged; };
 
-// kStore8All: the staged epilogue calls store8_all(m, n, w, in_range, lane)
-// from every lane of every wave (with in_range false outside the matrix),
-// so the epilogue may combine values across lanes.
+// kStore8All: the staged epilogue calls store8_all(m, n, w, in_range, lane,
+// extra) from every lane of every wave (with in_range false outside the
+// matrix), so the epilogue may combine values across lanes; `extra` is what
+// the epilogue's extra(m, n, in_range) loaded for that chunk beforehand.
 template <class Epi, class = void>
 struct Store8All { static constexpr bool value = false; };
 template <class Epi>
@@ -415,14 +416,32 @@ __device__ __forceinline__ void g2_store_staged(char* smem, int bias_off,
   constexpr int kChunks = BM * BN / 8;
   static_assert(!Store8All<Epi>::value || kChunks % (64 * NW) == 0,
                 "store8_all needs every lane in every pass");
-  for (int c = tid; c < kChunks; c += 64 * NW) {
-    const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
-    const int m = m0 + rl, n = n0 + cl;
-    if constexpr (Store8All<Epi>::value)
+  if constexpr (Store8All<Epi>::value) {
+    // The epilogue's own operands (Epi::extra) of every pass are loaded first:
+    // inside the store loop each load would wait behind the previous pass's
+    // stores (they may alias), one memory latency per pass.
+    constexpr int kPass = kChunks / (64 * NW);
+    typename Epi::Extra ex[kPass];
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int c = tid + p * 64 * NW;
+      const int m = m0 + c / (BN / 8), n = n0 + (c % (BN / 8)) * 8;
+      ex[p] = epi.extra(m, n, m < M && n < N);
+    }
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int c = tid + p * 64 * NW;
+      const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+      const int m = m0 + rl, n = n0 + cl;
       epi.store8_all(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl), m < M && n < N,
-                     lane);
-    else if (m < M && n < N)
-      epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
+                     lane, ex[p]);
+    }
+  } else {
+    for (int c = tid; c < kChunks; c += 64 * NW) {
+      const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+      const int m = m0 + rl, n = n0 + cl;
+      if (m < M && n < N) epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
+    }
   }
 }
 
