@@ -323,6 +323,18 @@ struct Store8All<Epi, decltype(void(Epi::kStore8All))> {
   static constexpr bool value = Epi::kStore8All;
 };
 
+// Extra: a direct epilogue that reads memory per 4-column run (a residual, a
+// bias) declares Epi::Extra and extra(m, n, in_range); the kernel loads the
+// runs of all its (i, j, g) first and then calls epi(m, n, v, extra) for
+// each: loads issued between the stores would each wait for the previous
+// stores (they may alias, and stores count in vmcnt).
+template <class Epi, class = void>
+struct HasExtra { static constexpr bool value = false; };
+template <class Epi>
+struct HasExtra<Epi, decltype(void(sizeof(typename Epi::Extra)))> {
+  static constexpr bool value = true;
+};
+
 template <class Epi, class = void>
 struct SplitOffsets { static constexpr bool value = false; };
 template <class Epi>
@@ -541,6 +553,34 @@ void gemm2_kernel(
   } else {
     static_assert(!Store8All<Epi>::value, "store8_all epilogues need the staged path");
     // ---- epilogue straight from the D^T accumulators
+    if constexpr (HasExtra<Epi>::value && !SplitOffsets<Epi>::value) {
+      typename Epi::Extra ex[MT][NT][4];
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+            const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+            ex[i][j][g] = epi.extra(m, n, m < M && n < N);
+          }
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+            const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+            if (m < M && n < N) {
+              const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                  acc[i][j][4 * g + 3]};
+              epi(m, n, v, ex[i][j][g]);
+            }
+          }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int m = m0 + wm * WTM + i * 32 + (lane & 31);

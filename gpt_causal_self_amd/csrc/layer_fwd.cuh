@@ -14,23 +14,40 @@ namespace gpt_attn {
 // c_proj epilogue with the Block's residual: out = acc + bias + res, one
 // rounding (page "nanoGPT global flow walkthrough", section 2.5: the attention
 // output is added back onto x).  Stored straight from the accumulators.
+// The residual and bias runs of columns n..n+3 of row m (zeros where absent).
+struct ResBias {
+  uint2 r, b;
+};
+__device__ __forceinline__ ResBias load_res_bias(const bf16_t* res, const bf16_t* bias, int ldc,
+                                                 int m, int n, bool ok) {
+  ResBias e{make_uint2(0u, 0u), make_uint2(0u, 0u)};
+  if (ok) {
+    if (res) e.r = *reinterpret_cast<const uint2*>(res + (size_t)m * ldc + n);
+    if (bias) e.b = *reinterpret_cast<const uint2*>(bias + n);
+  }
+  return e;
+}
+
 struct Epi2RowMajorRes {
   bf16_t* out;
   int ldc;
   const bf16_t* bias;  // may be NULL
   const bf16_t* res;   // [M][ldc]
-  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
-    float b[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
-      const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
-      b[0] = bf2f(u.x & 0xffff); b[1] = bf2f(u.x >> 16);
-      b[2] = bf2f(u.y & 0xffff); b[3] = bf2f(u.y >> 16);
-    }
-    const uint2 r = *reinterpret_cast<const uint2*>(res + (size_t)m * ldc + n);
+  typedef ResBias Extra;
+  __device__ __forceinline__ Extra extra(int m, int n, bool ok) const {
+    return load_res_bias(res, bias, ldc, m, n, ok);
+  }
+  __device__ __forceinline__ void operator()(int m, int n, const float* v, const Extra& e) const {
+    const uint2 r = e.r, u = e.b;
     uint2 w;
-    w.x = pack_bf16x2(v[0] + b[0] + bf2f(r.x & 0xffff), v[1] + b[1] + bf2f(r.x >> 16));
-    w.y = pack_bf16x2(v[2] + b[2] + bf2f(r.y & 0xffff), v[3] + b[3] + bf2f(r.y >> 16));
+    w.x = pack_bf16x2(v[0] + bf2f(u.x & 0xffff) + bf2f(r.x & 0xffff),
+                      v[1] + bf2f(u.x >> 16) + bf2f(r.x >> 16));
+    w.y = pack_bf16x2(v[2] + bf2f(u.y & 0xffff) + bf2f(r.y & 0xffff),
+                      v[3] + bf2f(u.y >> 16) + bf2f(r.y >> 16));
     *reinterpret_cast<uint2*>(out + (size_t)m * ldc + n) = w;
+  }
+  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
+    (*this)(m, n, v, extra(m, n, true));
   }
 };
 
@@ -42,19 +59,18 @@ struct Epi2RowMajorDrop {
   const bf16_t* bias;  // may be NULL
   const bf16_t* res;   // may be NULL
   DropParams drop;
+  typedef ResBias Extra;
+  __device__ __forceinline__ Extra extra(int m, int n, bool ok) const {
+    return load_res_bias(res, bias, ldc, m, n, ok);
+  }
   __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
-    float b[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
-      const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
-      b[0] = bf2f(u.x & 0xffff); b[1] = bf2f(u.x >> 16);
-      b[2] = bf2f(u.y & 0xffff); b[3] = bf2f(u.y >> 16);
-    }
-    float r[4] = {0.f, 0.f, 0.f, 0.f};
-    if (res) {
-      const uint2 u = *reinterpret_cast<const uint2*>(res + (size_t)m * ldc + n);
-      r[0] = bf2f(u.x & 0xffff); r[1] = bf2f(u.x >> 16);
-      r[2] = bf2f(u.y & 0xffff); r[3] = bf2f(u.y >> 16);
-    }
+    (*this)(m, n, v, extra(m, n, true));
+  }
+  __device__ __forceinline__ void operator()(int m, int n, const float* v, const Extra& e) const {
+    const float b[4] = {bf2f(e.b.x & 0xffff), bf2f(e.b.x >> 16), bf2f(e.b.y & 0xffff),
+                        bf2f(e.b.y >> 16)};
+    const float r[4] = {bf2f(e.r.x & 0xffff), bf2f(e.r.x >> 16), bf2f(e.r.y & 0xffff),
+                        bf2f(e.r.y >> 16)};
     // columns n..n+3 (n % 4 == 0): one Philox call
     const uint4 w = philox4x32_10(make_uint4((uint32_t)n >> 2, (uint32_t)m, 0u, 2u), drop.k0,
                                   drop.k1);
