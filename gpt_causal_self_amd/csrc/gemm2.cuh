@@ -59,6 +59,16 @@ __device__ __forceinline__ void bar_nofence() {
   asm volatile("" ::: "memory");
 }
 
+// s_barrier after this wave's LDS writes have completed (lgkmcnt 0): the
+// barrier alone does not order one wave's ds_write before another wave's
+// ds_read of the same address.
+__device__ __forceinline__ void bar_after_lds_writes() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int BM, int BN, int BK, int NSTAGE, bool A_KC, bool B_KC, int NW = 4>
 struct Gemm2Cfg {
   static_assert(BK == 64 || BK == 32, "BK");
@@ -323,16 +333,18 @@ struct Store8All<Epi, decltype(void(Epi::kStore8All))> {
   static constexpr bool value = Epi::kStore8All;
 };
 
-// Extra: a direct epilogue that reads memory per 4-column run (a residual, a
-// bias) declares Epi::Extra and extra(m, n, in_range); the kernel loads the
-// runs of all its (i, j, g) first and then calls epi(m, n, v, extra) for
-// each: loads issued between the stores would each wait for the previous
-// stores (they may alias, and stores count in vmcnt).
+// kStagedF32: the staged epilogue keeps acc + bias in fp32 (one half of the
+// tile's rows at a time, so the fp32 half-tile fits the ring's LDS) and hands
+// each 8-column run to store8f(m, n, v[8], extra) to round once.  Such an
+// epilogue reads memory per run (a residual): it declares Epi::Extra8 and
+// extra8(m, n, in_range), and the runs of all passes are loaded before the
+// first store, since a load issued between stores waits for them (they may
+// alias, and stores count in vmcnt).
 template <class Epi, class = void>
-struct HasExtra { static constexpr bool value = false; };
+struct StagedF32 { static constexpr bool value = false; };
 template <class Epi>
-struct HasExtra<Epi, decltype(void(sizeof(typename Epi::Extra)))> {
-  static constexpr bool value = true;
+struct StagedF32<Epi, decltype(void(Epi::kStagedF32))> {
+  static constexpr bool value = Epi::kStagedF32;
 };
 
 template <class Epi, class = void>
@@ -424,7 +436,7 @@ __device__ __forceinline__ void g2_store_staged(char* smem, int bias_off,
         *reinterpret_cast<uint2*>(ct + rl * SP + cl) = w;
       }
     }
-  bar_nofence();
+  bar_after_lds_writes();
   constexpr int kChunks = BM * BN / 8;
   static_assert(!Store8All<Epi>::value || kChunks % (64 * NW) == 0,
                 "store8_all needs every lane in every pass");
@@ -457,6 +469,66 @@ __device__ __forceinline__ void g2_store_staged(char* smem, int bias_off,
   }
 }
 
+// Staged epilogue in fp32 for kStagedF32 epilogues: for each wave row h of
+// the WGM, the waves of that row write acc + bias (fp32) into an LDS tile
+// [BM / WGM][BN + 4]; then all threads read 8-column runs (two 16-byte reads),
+// with the epilogue's Extra8 of all passes loaded first, and call store8f.
+template <int BM, int BN, int WGM, int WGN, class Epi>
+__device__ __forceinline__ void g2_store_staged_f32(
+    char* smem, int bias_off, const floatx16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+    const Epi& epi, int m0, int n0, int M, int N, int tid, int wm, int wn) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MT = WTM / 32, NT = WTN / 32;
+  constexpr int SP = BN + 4;                       // pitch (floats); 16-byte aligned rows
+  constexpr int kChunks = WTM * BN / 8;            // 8-column runs of one wave row
+  constexpr int kPass = (kChunks + 64 * NW - 1) / (64 * NW);
+  const int lane = tid & 63;
+  float* ct = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int h = 0; h < WGM; ++h) {
+    bar_nofence();  // the ring (h = 0) or the previous half's runs are read
+    if (wm == h) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int cl = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+          const uint2 bu = *reinterpret_cast<const uint2*>(smem + bias_off + cl * 2);
+          const float b[4] = {bf2f(bu.x & 0xffff), bf2f(bu.x >> 16), bf2f(bu.y & 0xffff),
+                              bf2f(bu.y >> 16)};
+#pragma unroll
+          for (int i = 0; i < MT; ++i) {
+            const int rl = i * 32 + (lane & 31);
+            *reinterpret_cast<float4*>(ct + rl * SP + cl) =
+                make_float4(acc[i][j][4 * g] + b[0], acc[i][j][4 * g + 1] + b[1],
+                            acc[i][j][4 * g + 2] + b[2], acc[i][j][4 * g + 3] + b[3]);
+          }
+        }
+    }
+    bar_after_lds_writes();
+    typename Epi::Extra8 ex[kPass];
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int c = tid + p * 64 * NW;
+      const int m = m0 + h * WTM + c / (BN / 8), n = n0 + (c % (BN / 8)) * 8;
+      ex[p] = epi.extra8(m, n, c < kChunks && m < M && n < N);
+    }
+#pragma unroll
+    for (int p = 0; p < kPass; ++p) {
+      const int c = tid + p * 64 * NW;
+      const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+      const int m = m0 + h * WTM + rl, n = n0 + cl;
+      if (c < kChunks && m < M && n < N) {
+        const float4 a = *reinterpret_cast<const float4*>(ct + rl * SP + cl);
+        const float4 b = *reinterpret_cast<const float4*>(ct + rl * SP + cl + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        epi.store8f(m, n, v, ex[p]);
+      }
+    }
+  }
+}
+
 // OCC: waves per SIMD the register allocation must allow (1 = no limit
 // beyond the block size).
 template <int BM, int BN, int BK, int NSTAGE, bool A_KC, bool B_KC, int WGM, int WGN, class Epi,
@@ -471,10 +543,12 @@ void gemm2_kernel(
   constexpr int MT = WTM / 32, NT = WTN / 32;
   // A staging epilogue reuses the ring's LDS, grown to the output tile when
   // that still fits the CU's 160 KB.
-  constexpr int kEpiBytes = Staged<Epi>::value ? BM * (BN + 8) * 2 : 0;
+  constexpr int kEpiBytes = StagedF32<Epi>::value ? (BM / WGM) * (BN + 4) * 4
+                            : Staged<Epi>::value   ? BM * (BN + 8) * 2
+                                                   : 0;
   constexpr int kSmemAll =
       kEpiBytes > Cfg::kSmem && kEpiBytes + BN * 2 <= 160 * 1024 ? kEpiBytes : Cfg::kSmem;
-  constexpr bool kStagedEpi = Staged<Epi>::value && BM * (BN + 8) * 2 <= kSmemAll;
+  constexpr bool kStagedEpi = Staged<Epi>::value && kEpiBytes <= kSmemAll;
   // The staged epilogue reads the tile's bias columns from LDS, placed after
   // the ring / staging area.
   constexpr int kBiasOff = (kSmemAll + 15) / 16 * 16;
@@ -549,38 +623,13 @@ void gemm2_kernel(
   }
 
   if constexpr (kStagedEpi) {
-    g2_store_staged<BM, BN, WGM, WGN>(smem, kBiasOff, acc, epi, m0, n0, M, N, tid, wm, wn);
+    if constexpr (StagedF32<Epi>::value)
+      g2_store_staged_f32<BM, BN, WGM, WGN>(smem, kBiasOff, acc, epi, m0, n0, M, N, tid, wm, wn);
+    else
+      g2_store_staged<BM, BN, WGM, WGN>(smem, kBiasOff, acc, epi, m0, n0, M, N, tid, wm, wn);
   } else {
     static_assert(!Store8All<Epi>::value, "store8_all epilogues need the staged path");
     // ---- epilogue straight from the D^T accumulators
-    if constexpr (HasExtra<Epi>::value && !SplitOffsets<Epi>::value) {
-      typename Epi::Extra ex[MT][NT][4];
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int m = m0 + wm * WTM + i * 32 + (lane & 31);
-            const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-            ex[i][j][g] = epi.extra(m, n, m < M && n < N);
-          }
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int m = m0 + wm * WTM + i * 32 + (lane & 31);
-            const int n = n0 + wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
-            if (m < M && n < N) {
-              const float v[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                                  acc[i][j][4 * g + 3]};
-              epi(m, n, v, ex[i][j][g]);
-            }
-          }
-      return;
-    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       const int m = m0 + wm * WTM + i * 32 + (lane & 31);

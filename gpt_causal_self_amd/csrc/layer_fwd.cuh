@@ -11,78 +11,114 @@
 
 namespace gpt_attn {
 
-// c_proj epilogue with the Block's residual: out = acc + bias + res, one
-// rounding (page "nanoGPT global flow walkthrough", section 2.5: the attention
-// output is added back onto x).  Stored straight from the accumulators.
-// The residual and bias runs of columns n..n+3 of row m (zeros where absent).
-struct ResBias {
-  uint2 r, b;
-};
-__device__ __forceinline__ ResBias load_res_bias(const bf16_t* res, const bf16_t* bias, int ldc,
-                                                 int m, int n, bool ok) {
-  ResBias e{make_uint2(0u, 0u), make_uint2(0u, 0u)};
-  if (ok) {
-    if (res) e.r = *reinterpret_cast<const uint2*>(res + (size_t)m * ldc + n);
-    if (bias) e.b = *reinterpret_cast<const uint2*>(bias + n);
+// bf16 residual run of 8 columns as fp32 helpers
+__device__ __forceinline__ void bf16x8_to_f32(uint4 u, float* f) {
+  const unsigned w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f[2 * e] = bf2f(w[e] & 0xffff);
+    f[2 * e + 1] = bf2f(w[e] >> 16);
   }
-  return e;
 }
 
+// c_proj epilogue with the Block's residual (page "nanoGPT global flow
+// walkthrough", section 2.5: the attention output is added back onto x):
+// out = bf16(acc + bias + res), one rounding.  Through the GEMM's fp32
+// staged epilogue (coalesced 16-byte runs; the residual runs of all passes
+// are loaded before the stores) or called per 4 columns (split-K finish,
+// short-sequence path).
 struct Epi2RowMajorRes {
   bf16_t* out;
   int ldc;
   const bf16_t* bias;  // may be NULL
   const bf16_t* res;   // [M][ldc]
-  typedef ResBias Extra;
-  __device__ __forceinline__ Extra extra(int m, int n, bool ok) const {
-    return load_res_bias(res, bias, ldc, m, n, ok);
+  static constexpr bool kStaged = true;
+  static constexpr bool kStagedF32 = true;
+  __device__ __forceinline__ const bf16_t* bias_ptr() const { return bias; }
+  typedef uint4 Extra8;
+  __device__ __forceinline__ Extra8 extra8(int m, int n, bool ok) const {
+    return ok ? *reinterpret_cast<const uint4*>(res + (size_t)m * ldc + n)
+              : make_uint4(0u, 0u, 0u, 0u);
   }
-  __device__ __forceinline__ void operator()(int m, int n, const float* v, const Extra& e) const {
-    const uint2 r = e.r, u = e.b;
-    uint2 w;
-    w.x = pack_bf16x2(v[0] + bf2f(u.x & 0xffff) + bf2f(r.x & 0xffff),
-                      v[1] + bf2f(u.x >> 16) + bf2f(r.x >> 16));
-    w.y = pack_bf16x2(v[2] + bf2f(u.y & 0xffff) + bf2f(r.y & 0xffff),
-                      v[3] + bf2f(u.y >> 16) + bf2f(r.y >> 16));
-    *reinterpret_cast<uint2*>(out + (size_t)m * ldc + n) = w;
+  // v: acc + bias of columns n .. n+7
+  __device__ __forceinline__ void store8f(int m, int n, const float* v, const Extra8& r) const {
+    float x[8];
+    bf16x8_to_f32(r, x);
+    uint4 o;
+    o.x = pack_bf16x2(v[0] + x[0], v[1] + x[1]);
+    o.y = pack_bf16x2(v[2] + x[2], v[3] + x[3]);
+    o.z = pack_bf16x2(v[4] + x[4], v[5] + x[5]);
+    o.w = pack_bf16x2(v[6] + x[6], v[7] + x[7]);
+    *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = o;
   }
   __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
-    (*this)(m, n, v, extra(m, n, true));
+    float b[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+      const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
+      b[0] = bf2f(u.x & 0xffff); b[1] = bf2f(u.x >> 16);
+      b[2] = bf2f(u.y & 0xffff); b[3] = bf2f(u.y >> 16);
+    }
+    const uint2 r = *reinterpret_cast<const uint2*>(res + (size_t)m * ldc + n);
+    uint2 w;
+    w.x = pack_bf16x2(v[0] + b[0] + bf2f(r.x & 0xffff), v[1] + b[1] + bf2f(r.x >> 16));
+    w.y = pack_bf16x2(v[2] + b[2] + bf2f(r.y & 0xffff), v[3] + b[3] + bf2f(r.y >> 16));
+    *reinterpret_cast<uint2*>(out + (size_t)m * ldc + n) = w;
   }
 };
 
 // c_proj epilogue with dropout on the c_proj output (philox.cuh) and an
-// optional residual: out = res + keep * (acc + bias) / (1 - p), one rounding.
+// optional residual: out = res + keep * (acc + bias) / (1 - p), one rounding;
+// staged in fp32 like Epi2RowMajorRes, or called per 4 columns.  One Philox
+// call per 4 columns.
 struct Epi2RowMajorDrop {
   bf16_t* out;
   int ldc;
   const bf16_t* bias;  // may be NULL
   const bf16_t* res;   // may be NULL
   DropParams drop;
-  typedef ResBias Extra;
-  __device__ __forceinline__ Extra extra(int m, int n, bool ok) const {
-    return load_res_bias(res, bias, ldc, m, n, ok);
+  static constexpr bool kStaged = true;
+  static constexpr bool kStagedF32 = true;
+  __device__ __forceinline__ const bf16_t* bias_ptr() const { return bias; }
+  typedef uint4 Extra8;
+  __device__ __forceinline__ Extra8 extra8(int m, int n, bool ok) const {
+    return (ok && res) ? *reinterpret_cast<const uint4*>(res + (size_t)m * ldc + n)
+                       : make_uint4(0u, 0u, 0u, 0u);
   }
-  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
-    (*this)(m, n, v, extra(m, n, true));
-  }
-  __device__ __forceinline__ void operator()(int m, int n, const float* v, const Extra& e) const {
-    const float b[4] = {bf2f(e.b.x & 0xffff), bf2f(e.b.x >> 16), bf2f(e.b.y & 0xffff),
-                        bf2f(e.b.y >> 16)};
-    const float r[4] = {bf2f(e.r.x & 0xffff), bf2f(e.r.x >> 16), bf2f(e.r.y & 0xffff),
-                        bf2f(e.r.y >> 16)};
+  // out[m][n .. n+3] = r + keep * a * scale for 4 values a (bias included)
+  __device__ __forceinline__ uint2 apply4(int m, int n, const float* a, const float* r) const {
     // columns n..n+3 (n % 4 == 0): one Philox call
     const uint4 w = philox4x32_10(make_uint4((uint32_t)n >> 2, (uint32_t)m, 0u, 2u), drop.k0,
                                   drop.k1);
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
     float o[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = r[e] + (wd[e] >= drop.thresh ? (v[e] + b[e]) * drop.scale : 0.f);
+    for (int e = 0; e < 4; ++e) o[e] = r[e] + (wd[e] >= drop.thresh ? a[e] * drop.scale : 0.f);
     uint2 st;
     st.x = pack_bf16x2(o[0], o[1]);
     st.y = pack_bf16x2(o[2], o[3]);
-    *reinterpret_cast<uint2*>(out + (size_t)m * ldc + n) = st;
+    return st;
+  }
+  // v: acc + bias of columns n .. n+7
+  __device__ __forceinline__ void store8f(int m, int n, const float* v, const Extra8& rr) const {
+    float x[8];
+    bf16x8_to_f32(rr, x);
+    const uint2 lo = apply4(m, n, v, x), hi = apply4(m, n + 4, v + 4, x + 4);
+    *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
+    float a[4] = {v[0], v[1], v[2], v[3]};
+    if (bias) {
+      const uint2 u = *reinterpret_cast<const uint2*>(bias + n);
+      a[0] += bf2f(u.x & 0xffff); a[1] += bf2f(u.x >> 16);
+      a[2] += bf2f(u.y & 0xffff); a[3] += bf2f(u.y >> 16);
+    }
+    float r[4] = {0.f, 0.f, 0.f, 0.f};
+    if (res) {
+      const uint2 u = *reinterpret_cast<const uint2*>(res + (size_t)m * ldc + n);
+      r[0] = bf2f(u.x & 0xffff); r[1] = bf2f(u.x >> 16);
+      r[2] = bf2f(u.y & 0xffff); r[3] = bf2f(u.y >> 16);
+    }
+    *reinterpret_cast<uint2*>(out + (size_t)m * ldc + n) = apply4(m, n, a, r);
   }
 };
 
