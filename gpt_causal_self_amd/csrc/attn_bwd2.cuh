@@ -20,6 +20,7 @@
 #include "attn_fwd.cuh"
 #include "common.cuh"
 #include "gemm2.cuh"
+#include "keep_bits.cuh"
 #include "philox.cuh"
 
 namespace gpt_attn {
@@ -91,13 +92,15 @@ struct Epi2DgradRowStats {
 // (lane = query) and keeps q and dO of its query as MFMA B operands.  Per
 // 64-key tile: S^T = K Q^T and dP^T = V dO^T (keys on the MFMA rows),
 // P^T = exp2(S^T * scale * log2 e - L), dS^T = P^T (dP^T - D) (with DROP,
-// dP carries the keep factor z of the weight), dQ^T += K^T dS^T.
+// dP carries the keep factor z of the weight, read from the forward's keep
+// bits, query-major layout of keep_bits.cuh), dQ^T += K^T dS^T.
 template <int HS, bool DROP>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
     const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg,
     const bf16_t* __restrict__ Vg, const bf16_t* __restrict__ dOg,
     const float* __restrict__ Lpad, const float* __restrict__ Dpad, bf16_t* __restrict__ dqkv,
-    int H, int T, int Tpad, float scale, float scale_log2, DropParams drop) {
+    int H, int T, int Tpad, float scale, float scale_log2, DropParams drop,
+    const uint32_t* __restrict__ keepq) {
   static_assert(HS == 32 || HS == 64, "head size");
   constexpr int BKV = 64;
   constexpr int TILE = BKV * HS * 2;   // bytes of one K or V tile
@@ -192,8 +195,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((address_space(3))) const bf16x8 lds_b128;
 
+  // kw: this lane's keep bits of the tile (bit 16kt + 4g + e)
   auto tile = [&](auto mask_tag, const char* __restrict__ rd, char* __restrict__ wr, int jn,
-                  int j0) {
+                  int j0, uint32_t kw) {
     constexpr bool MASK = decltype(mask_tag)::value;
     if (jn >= 0) issue(wr, jn);
     const lds_char* lbase = (const lds_char*)rd;
@@ -218,18 +222,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        uint4 w = make_uint4(0u, 0u, 0u, 0u);
-        if constexpr (DROP)
-          w = philox4x32_10(make_uint4((uint32_t)(j0 + kt * 32 + 8 * g + 4 * hi) >> 2,
-                                       (uint32_t)myq, (uint32_t)bh, 1u),
-                            drop.k0, drop.k1);
-        const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
           const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][r], scale_log2, -L2));
           float dpv = dp[kt][r];
-          if constexpr (DROP) dpv *= wd[e] >= drop.thresh ? drop.scale : 0.f;
+          if constexpr (DROP) dpv *= ((kw >> (16 * kt + r)) & 1u) ? drop.scale : 0.f;
           float ds = p * (dpv - Dq);
           if constexpr (MASK) {
             const int key = j0 + kt * 32 + 8 * g + 4 * hi + e;
@@ -263,14 +261,27 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
       }
   };
 
+  // keep bits: the word of tile it + 1 is loaded during tile it (before its
+  // ring loads, so the next ring wait covers it)
+  const KeepBitsLayout kl(T);
+  uint32_t kw = 0;
+  if constexpr (DROP) kw = keepq[kl.q_index(bh, 0, hi, myq)];
+  auto next_keep = [&](int jn) -> uint32_t {
+    if constexpr (DROP) {
+      if (jn >= 0) return keepq[kl.q_index(bh, jn / BKV, hi, myq)];
+    }
+    return 0u;
+  };
   const int n_full = min(nkv, (qt * 128) / BKV);
   int it = 0;
   for (; it < n_full; ++it) {
     wait_vmcnt<0>();
     bar_nofence();
     const int jn = it + 1 < nkv ? (it + 1) * BKV : -1;
+    const uint32_t kn = next_keep(jn);
     tile(std::integral_constant<bool, false>{}, smem + (it & 1) * STAGE,
-         smem + ((it + 1) & 1) * STAGE, jn, it * BKV);
+         smem + ((it + 1) & 1) * STAGE, jn, it * BKV, kw);
+    kw = kn;
   }
   for (; it < nkv; ++it) {
     wait_vmcnt<0>();
@@ -278,10 +289,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
     const int jn = it + 1 < nkv ? (it + 1) * BKV : -1;
     const int j0 = it * BKV;
     char* wr = smem + ((it + 1) & 1) * STAGE;
+    const uint32_t kn = next_keep(jn);
     if (j0 <= q0 + 31)
-      tile(std::integral_constant<bool, true>{}, smem + (it & 1) * STAGE, wr, jn, j0);
+      tile(std::integral_constant<bool, true>{}, smem + (it & 1) * STAGE, wr, jn, j0, kw);
     else if (jn >= 0)
       issue(wr, jn);
+    kw = kn;
   }
 
   if (myq < T) {
@@ -303,7 +316,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
 // One block = 4 waves = 128 keys of one (b, h); wave w owns 32 keys (lane =
 // key) and keeps k and v of its key as MFMA B operands.  Per 64-query tile:
 // S = Q K^T and dP = dO V^T (queries on the MFMA rows), P = exp2(S * scale *
-// log2 e - L), dS = P (dP - D) (with DROP: P z for dV, dP z in dS),
+// log2 e - L), dS = P (dP - D) (with DROP: P z for dV, dP z in dS, the keep
+// factors z from the forward's keep bits, key-major layout of keep_bits.cuh),
 // dV^T += dO^T P and dK^T += Q^T dS.  Stage: Q tile, dO tile, then the 64
 // queries' L (log2 units) and D (fp32).
 template <int HS, bool DROP>
@@ -311,11 +325,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
     const bf16_t* __restrict__ Qg, const bf16_t* __restrict__ Kg,
     const bf16_t* __restrict__ Vg, const bf16_t* __restrict__ dOg,
     const float* __restrict__ Lpad, const float* __restrict__ Dpad, bf16_t* __restrict__ dqkv,
-    int H, int T, int Tpad, float scale, float scale_log2, DropParams drop) {
+    int H, int T, int Tpad, float scale, float scale_log2, DropParams drop,
+    const uint32_t* __restrict__ keepk) {
   static_assert(HS == 32 || HS == 64, "head size");
   constexpr int BQ = 64;
   constexpr int TILE = BQ * HS * 2;    // bytes of one Q or dO tile
-  constexpr int STAGE = 2 * TILE + 512;
+  // Q tile, dO tile, L and D of the 64 queries (512 B), and with DROP the
+  // keep words of the block's 128 keys for the tile (2 x 512 B)
+  constexpr int STAGE = 2 * TILE + 512 + (DROP ? 1024 : 0);
   constexpr int RB = HS * 2;
   constexpr int CPR = HS / 8;
   constexpr int RPI = 64 / CPR;
@@ -374,6 +391,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
   const int nqt = (T - kb0 + BQ - 1) / BQ;  // query tiles i0 = kb0, kb0 + 64, ...
   const float* Lrow = Lpad + (size_t)bh * Tpad;
   const float* Drow = Dpad + (size_t)bh * Tpad;
+  const KeepBitsLayout kl(T);
 
   // Loop-invariant per-lane (row, chunk) of each load; a query tile at i0
   // adds i0 rows.  Only a tile that crosses T checks rows.
@@ -407,6 +425,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
       const float* src = lane < 16 ? Lrow + i0 + 4 * lane : Drow + i0 + 4 * (lane - 16);
       __builtin_amdgcn_load_to_lds((void*)src, GA_LDS(dst + 2 * TILE), 16, 0, 0);
     }
+    // keep words k_index(bh, i0 / 64, hi, kb0 .. kb0 + 127) (keys padded to
+    // 128, so always in bounds): lane l of wave 1 fetches 4 keys of hi = l / 32
+    if constexpr (DROP) {
+      if (wid == 1) {
+        const uint32_t* src = keepk + kl.k_index(bh, i0 / BQ, lane >> 5, kb0 + 4 * (lane & 31));
+        __builtin_amdgcn_load_to_lds((void*)src, GA_LDS(dst + 2 * TILE + 512), 16, 0, 0);
+      }
+    }
   };
   issue(smem, kb0);
 
@@ -437,6 +463,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
       }
     }
     // lane = key mykey; register r of qh <-> query i0 + qh*32 + 8(r/4) + 4hi + r%4
+    // this lane's keep bits of the query tile (bit 16qh + 4g + e)
+    uint32_t kw = 0;
+    if constexpr (DROP)
+      kw = *(const __attribute__((address_space(3))) uint32_t*)(
+          lbase + 2 * TILE + 512 + (hi * 128 + (mykey - kb0)) * 4);
 #pragma unroll
     for (int qh = 0; qh < 2; ++qh) {
 #pragma unroll
@@ -445,36 +476,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
         const f4v Lv = *(lds_f4*)(lbase + 2 * TILE + ql * 4);
         const f4v Dv = *(lds_f4*)(lbase + 2 * TILE + 256 + ql * 4);
         const float Ls[4] = {Lv[0], Lv[1], Lv[2], Lv[3]}, Ds[4] = {Dv[0], Dv[1], Dv[2], Dv[3]};
-        uint32_t keepw[4] = {0u, 0u, 0u, 0u};
-        if constexpr (DROP) {
-          // The 4 lanes of a quad hold keys 4a..4a+3 (same counter word a)
-          // and need, for each of the 4 queries of this register group, their
-          // own word of that query's Philox block: lane t computes the block
-          // of query ql + t, then a 4 x 4 transpose inside the quad (select
-          // word t ^ r, move it across lane distance r) hands every lane its
-          // word of every block.
-          const int t = lane & 3;
-          const uint4 w = philox4x32_10(
-              make_uint4((uint32_t)mykey >> 2, (uint32_t)(i0 + ql + t), (uint32_t)bh, 1u), drop.k0,
-              drop.k1);
-          const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-          uint32_t got[4];  // got[r]: word for this key of query ql + (t ^ r)
-          got[0] = wv[t];
-#pragma unroll
-          for (int r = 1; r < 4; ++r) {
-            const int si = t ^ r;
-            const uint32_t x = si == 0 ? wv[0] : si == 1 ? wv[1] : si == 2 ? wv[2] : wv[3];
-            // quad_perm xor 1, 2, 3: [1,0,3,2], [2,3,0,1], [3,2,1,0]
-            got[r] = (uint32_t)(r == 1   ? __builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false)
-                                : r == 2 ? __builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false)
-                                         : __builtin_amdgcn_update_dpp(0, (int)x, 0x1B, 0xF, 0xF, false));
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = e ^ t;
-            keepw[e] = r == 0 ? got[0] : r == 1 ? got[1] : r == 2 ? got[2] : got[3];
-          }
-        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
@@ -482,7 +483,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
           float p = __builtin_amdgcn_exp2f(fmaf(s[qh][r], scale_log2, -Ls[e]));
           float dpv = dp[qh][r];
           if constexpr (DROP) {
-            const float z = keepw[e] >= drop.thresh ? drop.scale : 0.f;
+            const float z = ((kw >> (16 * qh + r)) & 1u) ? drop.scale : 0.f;
             s[qh][r] = p * z;
             dp[qh][r] = p * (dpv * z - Ds[e]);
           } else {

@@ -30,6 +30,7 @@
 
 #include "common.cuh"
 #include "gemm2.cuh"
+#include "keep_bits.cuh"
 #include "philox.cuh"
 
 namespace gpt_attn {
@@ -76,12 +77,16 @@ __device__ __forceinline__ int tr_off(int off, int t) {
 
 // DROP: dropout on the attention weights (philox.cuh): the row sum uses
 // every weight, the P.V product only the kept ones, and the output is scaled
-// by 1 / (1 - p).
+// by 1 / (1 - p).  With keepq / keepk (a forward whose state the backward
+// uses) the keep decisions are also stored, one bit per weight, in the two
+// layouts of keep_bits.cuh, so that the backward reads them instead of
+// drawing the generator again.
 template <int HS, int NS, bool DROP = false>
 __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ Kg,
     const bf16_t* __restrict__ Vg, bf16_t* __restrict__ O, float* __restrict__ lse,
-    int H, int T, float scale_log2, DropParams drop = {}) {
+    int H, int T, float scale_log2, DropParams drop = {}, uint32_t* __restrict__ keepq = nullptr,
+    uint16_t* __restrict__ keepk = nullptr) {
   static_assert(HS == 32 || HS == 64, "head size");
   constexpr int BKV = kAttnBK;
   constexpr int TILE = BKV * HS * 2;   // bytes of one K or V tile
@@ -187,6 +192,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
   typedef __attribute__((address_space(3))) char lds_char;
   typedef __attribute__((address_space(3))) const bf16x8 lds_b128;
 
+  // Keep bits of the last tile this wave computed, stored at the start of the
+  // next tile (before its ring loads, so the ring's vmcnt waits find them
+  // long complete) or after the loop.
+  const KeepBitsLayout kl(T);
+  const bool store_keep = DROP && keepq != nullptr;
+  uint32_t pend_q = 0, pend_k = 0;
+  int pend_jt = -1;
+  auto flush_keep = [&]() {
+    if (store_keep && pend_jt >= 0) {
+      keepq[kl.q_index(bh, pend_jt, hi, myq)] = pend_q;
+      const size_t k0 = kl.k_index(bh, q0 >> 6, 0, pend_jt * 64 + lane);
+      const int qh = (q0 >> 5) & 1;
+      keepk[2 * k0 + qh] = (uint16_t)pend_k;
+      keepk[2 * (k0 + kl.Tk) + qh] = (uint16_t)(pend_k >> 16);
+      pend_jt = -1;
+    }
+  };
+
   // One 64-key tile held in ring stage rd; first issues the loads of the tile
   // at key jn into stage wr (when jn >= 0).  MASK: apply the causal mask
   // (diagonal tiles).  rd and wr are distinct stages: the restrict qualifiers
@@ -195,6 +218,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
   auto tile = [&](auto mask_tag, const char* __restrict__ rd, char* __restrict__ wr, int jn,
                   int j0) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    if constexpr (DROP) flush_keep();
     if (jn >= 0) issue(wr, jn);
     const lds_char* lbase = (const lds_char*)rd;
     // ---- S^T = K Q^T for keys j0 .. j0+63
@@ -256,7 +280,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     l += rs;
     if constexpr (DROP) {
       // keys j0 + kt*32 + 8g + 4hi + e (e = 0..3) of query myq: one Philox
-      // call covers the 4 consecutive keys of register group g
+      // call covers the 4 consecutive keys of register group g.  wq: this
+      // lane's keep bits (bit 16kt + 4g + e).
+      uint32_t wq = 0;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -264,11 +290,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
           const uint32_t jb = (uint32_t)(j0 + kt * 32 + 8 * g + 4 * hi);
           const uint4 w = philox4x32_10(make_uint4(jb >> 2, (uint32_t)myq, (uint32_t)bh, 1u),
                                         drop.k0, drop.k1);
-          if (w.x < drop.thresh) sc[kt][4 * g + 0] = 0.f;
-          if (w.y < drop.thresh) sc[kt][4 * g + 1] = 0.f;
-          if (w.z < drop.thresh) sc[kt][4 * g + 2] = 0.f;
-          if (w.w < drop.thresh) sc[kt][4 * g + 3] = 0.f;
+          const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool kp = wd[e] >= drop.thresh;
+            if (!kp) sc[kt][4 * g + e] = 0.f;
+            wq |= (uint32_t)kp << (16 * kt + 4 * g + e);
+          }
         }
+      if (store_keep) {
+        // lane o: keep bits of key j0 + o over the wave's 32 queries
+        const uint32_t xk = keep_transpose(wq);
+        pend_q = wq;
+        pend_k = keep_half16(xk) | (keep_half16(xk >> 4) << 16);
+        pend_jt = j0 >> 6;
+      }
     }
     // ---- O^T += V^T P^T; V^T operand by transposing reads in the key order
     // of the P registers: element e <-> key kb + 8(e/4) + 4*hi + e%4.
@@ -324,6 +360,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     else if (jn >= 0)
       issue(wr, jn);
   }
+
+  if constexpr (DROP) flush_keep();
 
   if (myq < T) {
     const float inv = (DROP ? drop.scale : 1.f) / l;

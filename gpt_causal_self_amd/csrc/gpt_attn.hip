@@ -110,6 +110,7 @@ int gpt_attn_destroy(gpt_attn_t h) {
     if (hipDeviceSynchronize() != hipSuccess) rc = GPT_ATTN_ERR_HIP;
     if (hipFree(h->ws) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   }
+  if (h->keepq && hipFree(h->keepq) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   if (h->ev_fork && hipEventDestroy(h->ev_fork) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   if (h->ev_mid && hipEventDestroy(h->ev_mid) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   if (h->ev_join && hipEventDestroy(h->ev_join) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
@@ -179,9 +180,11 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
 
   if (h->dtype == GPT_ATTN_BF16) {
     const DropParams drop = make_drop(h->drop_p, h->drop_seed);
+    const bool keep = h->drop_p > 0.f && save_for_backward;
     layer_forward_bf16(h, (const bf16_t*)x, B, T, (const bf16_t*)W_attn, (const bf16_t*)b_attn,
                        (const bf16_t*)W_proj, (const bf16_t*)b_proj, (bf16_t*)y, nullptr, lse,
-                       st, h->drop_p > 0.f ? &drop : nullptr);
+                       st, h->drop_p > 0.f ? &drop : nullptr, keep ? h->keepq : nullptr,
+                       keep ? h->keepk : nullptr);
   } else {
     const float* xf = (const float*)x;
     float* qkv = (float*)h->qkv;
@@ -218,6 +221,20 @@ int gpt_attn_forward(gpt_attn_t h, const void* x, int B, int T, const void* W_at
 int gpt_attn_set_dropout(gpt_attn_t h, float p, unsigned long long seed) {
   if (!h || !(p >= 0.f && p < 1.f)) return GPT_ATTN_ERR_INVALID_ARG;
   if (p > 0.f && h->dtype != GPT_ATTN_BF16) return GPT_ATTN_ERR_UNSUPPORTED;
+  if (p > 0.f && !h->keepq) {
+    const KeepBitsLayout kl(h->max_T);
+    const size_t bh = (size_t)h->max_B * h->H;
+    const size_t qb = align_up(kl.q_words((int)bh) * sizeof(uint32_t));
+    const size_t kb = kl.k_words((int)bh) * sizeof(uint32_t);
+    void* buf = nullptr;
+    const hipError_t e = hipMalloc(&buf, qb + kb);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      return e == hipErrorOutOfMemory ? GPT_ATTN_ERR_OOM : GPT_ATTN_ERR_HIP;
+    }
+    h->keepq = (uint32_t*)buf;
+    h->keepk = (uint16_t*)((char*)buf + qb);
+  }
   h->drop_p = p;
   h->drop_seed = seed;
   return GPT_ATTN_OK;
@@ -346,28 +363,34 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     if (hs == 64) {
       if (drop) {
         hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<64, true>), kgrid2, dim3(256), 0, st, q,
-                           k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
+                           k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp,
+                           (const uint32_t*)h->keepk);
         hipLaunchKernelGGL((attn_bwd_dq2_bf16_kernel<64, true>), qgrid2, dim3(256), 0, st, q, k,
-                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
+                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp,
+                           (const uint32_t*)h->keepq);
       } else {
         hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<64, false>), kgrid2, dim3(256), 0, st, q,
                            k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2,
-                           DropParams{});
+                           DropParams{}, nullptr);
         hipLaunchKernelGGL((attn_bwd_dq2_bf16_kernel<64, false>), qgrid2, dim3(256), 0, st, q, k,
-                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, DropParams{});
+                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, DropParams{},
+                           nullptr);
       }
     } else {
       if (drop) {
         hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<32, true>), kgrid2, dim3(256), 0, st, q,
-                           k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
+                           k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp,
+                           (const uint32_t*)h->keepk);
         hipLaunchKernelGGL((attn_bwd_dq2_bf16_kernel<32, true>), qgrid2, dim3(256), 0, st, q, k,
-                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp);
+                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, dp,
+                           (const uint32_t*)h->keepq);
       } else {
         hipLaunchKernelGGL((attn_bwd_dkdv2_bf16_kernel<32, false>), kgrid2, dim3(256), 0, st, q,
                            k, v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2,
-                           DropParams{});
+                           DropParams{}, nullptr);
         hipLaunchKernelGGL((attn_bwd_dq2_bf16_kernel<32, false>), qgrid2, dim3(256), 0, st, q, k,
-                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, DropParams{});
+                           v, dym, Lpad, Dpad, dqkv, H, T, Tpad, scale, scale_log2, DropParams{},
+                           nullptr);
       }
     }
     mark(h, 6, st);

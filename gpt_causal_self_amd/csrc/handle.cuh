@@ -75,6 +75,11 @@ struct gpt_attn_handle {
   unsigned long long drop_seed;
   float saved_drop_p;
   unsigned long long saved_drop_seed;
+  // keep bits of the attention-weight dropout (keep_bits.cuh) stored by a
+  // forward that keeps state, read by the backward; allocated when dropout
+  // is first switched on, sized for max_B and max_T
+  uint32_t* keepq;
+  uint16_t* keepk;
   // optional stage events (measurement hook)
   hipEvent_t ev[8];
   int n_ev;

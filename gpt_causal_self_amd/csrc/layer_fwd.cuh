@@ -215,12 +215,15 @@ inline void launch_proj(const gpt_attn_handle* h, const bf16_t* A, int lda, cons
 // c_attn GEMM -> fused causal attention -> c_proj GEMM on stream st.
 // residual == NULL: y = layer(x); else y = residual + layer(x).
 // lse != NULL: also store the softmax log-sum-exp rows for the backward.
-// drop != NULL: dropout on the attention weights and the c_proj output.
+// drop != NULL: dropout on the attention weights and the c_proj output;
+// keepq / keepk != NULL: also store the attention weights' keep bits
+// (keep_bits.cuh) for the backward.
 inline void layer_forward_bf16(const gpt_attn_handle* h, const bf16_t* x, int B, int T,
                                const bf16_t* W_attn, const bf16_t* b_attn,
                                const bf16_t* W_proj, const bf16_t* b_proj, bf16_t* y,
                                const bf16_t* residual, float* lse, hipStream_t st,
-                               const DropParams* drop = nullptr) {
+                               const DropParams* drop = nullptr, uint32_t* keepq = nullptr,
+                               uint16_t* keepk = nullptr) {
   const int C = h->C, H = h->H, hs = h->hs;
   const int M = B * T;
   const size_t head_elems = (size_t)B * H * T * hs;  // one of q, k, v
@@ -236,11 +239,11 @@ inline void layer_forward_bf16(const gpt_attn_handle* h, const bf16_t* x, int B,
     if (hs == 64)
       hipLaunchKernelGGL((attn_fwd2_bf16_kernel<64, GA_ATTN_STAGES, true>), agrid, dim3(256), 0,
                          st, qkv, qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T,
-                         scale_log2, *drop);
+                         scale_log2, *drop, keepq, keepk);
     else
       hipLaunchKernelGGL((attn_fwd2_bf16_kernel<32, GA_ATTN_STAGES, true>), agrid, dim3(256), 0,
                          st, qkv, qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T,
-                         scale_log2, *drop);
+                         scale_log2, *drop, keepq, keepk);
   } else if (hs == 64) {
     hipLaunchKernelGGL((attn_fwd2_bf16_kernel<64, GA_ATTN_STAGES>), agrid, dim3(256), 0, st,
                        qkv, qkv + head_elems, qkv + 2 * head_elems, o, lse, H, T, scale_log2,

@@ -128,9 +128,16 @@ int gpt_attn_backward(gpt_attn_t h, const void *x, const void *W_attn,
  * the exact gradient through the same masks (the upstream gradient of the
  * c_proj output is masked, rescaled and stored in bf16 before the c_proj
  * gradients).  Callers change the seed between steps.
+ * Such a forward also stores the attention weights' keep decisions, one bit
+ * per weight in two layouts, which the backward reads instead of drawing the
+ * generator again; the first call with p > 0 allocates that buffer on the
+ * handle's device, max_B*n_head*2*R*(ceil(max_T/64) + R/64)*4 bytes with
+ * R = max_T rounded up to 128 (37.7 MB at max_B 12, n_head 12, max_T 1024),
+ * freed by gpt_attn_destroy.
  * Applies to gpt_attn_forward and gpt_attn_block_forward (bf16), not to
  * decoding.  Errors: INVALID_ARG (NULL handle, p < 0, p >= 1 or NaN),
- * UNSUPPORTED (p > 0 on an fp32 handle). */
+ * UNSUPPORTED (p > 0 on an fp32 handle), OOM or HIP (that buffer; dropout
+ * then stays as it was). */
 int gpt_attn_set_dropout(gpt_attn_t h, float p, unsigned long long seed);
 
 /* Release the handle and its workspace (waits for the device first).
