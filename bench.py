@@ -192,12 +192,12 @@ def write_traffic(fetch_dir, write_dir):
            "copy_fetch_kib": fetch["copy"], "copy_write_kib": write["copy"], "kernels": {}}
     lines = ["# HBM traffic per launch: GPT-2 124M attention layer forward "
              "(B12 T1024 C768 H12 bf16)", "",
-             "Commands (from /tmp with TMPDIR=/tmp on one MI355X; repository at $R):", "", "```",
-             "timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -f csv -d $R/gpurun_out/pmc_fetch "
+             "Commands (from /tmp with TMPDIR=/tmp on one MI355X; repository at $R, profiler output under $OUT):", "", "```",
+             "timeout -s KILL 60 rocprofv3 --pmc FETCH_SIZE -f csv -d $OUT/pmc_fetch "
              "-- python3 $R/bench.py --pmc-run",
-             "timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -f csv -d $R/gpurun_out/pmc_write "
+             "timeout -s KILL 60 rocprofv3 --pmc WRITE_SIZE -f csv -d $OUT/pmc_write "
              "-- python3 $R/bench.py --pmc-run",
-             "python3 $R/bench.py --write-traffic $R/gpurun_out/pmc_fetch $R/gpurun_out/pmc_write",
+             "python3 $R/bench.py --write-traffic $OUT/pmc_fetch $OUT/pmc_write",
              "```", "",
              f"Calibration: a device copy of {COPY_BYTES} bytes reads FETCH_SIZE "
              f"{fetch['copy']:.1f} KiB and WRITE_SIZE {write['copy']:.1f} KiB, so each kernel's "
@@ -252,10 +252,10 @@ def write_util(run_dir):
             c[1] = max(c[1], v)
     lines = ["# MFMA, LDS and VALU utilisation per kernel: GPT-2 124M attention layer "
              "(B12 T1024 C768 H12 bf16), forward, training step and MLP", "",
-             "Commands (from /tmp with TMPDIR=/tmp on one MI355X; repository at $R):", "", "```",
-             f"timeout -s KILL 60 rocprofv3 --pmc {UTIL_COUNTERS} -f csv -d $R/gpurun_out/pmc_util "
+             "Commands (from /tmp with TMPDIR=/tmp on one MI355X; repository at $R, profiler output under $OUT):", "", "```",
+             f"timeout -s KILL 60 rocprofv3 --pmc {UTIL_COUNTERS} -f csv -d $OUT/pmc_util "
              "-- python3 $R/bench.py --pmc-run-all",
-             "python3 $R/bench.py --write-util $R/gpurun_out/pmc_util", "```", "",
+             "python3 $R/bench.py --write-util $OUT/pmc_util", "```", "",
              f"Sources digest: {sources_digest()}", "",
              "Per dispatch, averaged over dispatches, with A = GRBM_GUI_ACTIVE / "
              f"{XCD_NUM} (the counter sums the XCDs' active cycles): MFMA util = "
@@ -312,10 +312,10 @@ def write_kernel_stats(stats_dir, out_md):
         return n.replace("void gpt_attn::", "").replace("unsigned short", "bf16")
     lines = ["# Kernel trace: GPT-2 124M attention layer (B12 T1024 C768 H12 bf16), "
              "bench.py forward + training step", "",
-             "Command (from /tmp with TMPDIR=/tmp on one MI355X; repository at $R):", "", "```",
+             "Command (from /tmp with TMPDIR=/tmp on one MI355X; repository at $R, profiler output under $OUT):", "", "```",
              "timeout -k 10 300 rocprofv3 --kernel-trace --stats -f csv -d "
-             "$R/gpurun_out/ktrace -o run -- python3 $R/bench.py --steps 20 --warmup 5 --no-cpu",
-             f"python3 $R/bench.py --write-kernel-stats $R/gpurun_out/ktrace {os.path.basename(out_md)}",
+             "$OUT/ktrace -o run -- python3 $R/bench.py --steps 20 --warmup 5 --no-cpu",
+             f"python3 $R/bench.py --write-kernel-stats $OUT/ktrace {os.path.basename(out_md)}",
              "```", "", f"Sources digest: {sources_digest()}", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -609,8 +609,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer runs on a single device; see the sharding notes in DESIGN.md)",
-              file=sys.stderr)
+              "(the layer runs on a single device)", file=sys.stderr)
         sys.exit(2)
 
     if args.pmc_run_all:
