@@ -167,3 +167,32 @@ def test_dropout_backward(B, T, C, H, p, seed):
     sig = grad_gate.sigmas(bound_inp, r)
     for k in ("dx", "dW_attn", "db_attn", "dW_proj", "db_proj"):
         grad_gate.check(k, g[k], r[k], sig[k])
+
+
+def test_dropout_backward_below_the_handle_maxima():
+    """Dropout gradients on a handle created for larger B and T than the call
+    (the stored keep bits are laid out for the call's T inside a buffer sized
+    for the maxima), after a first training step at another shape on the same
+    handle, against the oracle's exact gradient through the same masks."""
+    import torch
+    C, H, p = 256, 4, 0.2
+    layer = ga.Layer(C, H, 3, 400, "bf16")
+    for (B, T, seed) in ((3, 400, 51), (2, 257, 52)):
+        inp = make_inputs(B, T, C, H, dtype="bf16", seed=T + seed, with_dY=True)
+        d = {k: to_torch(getattr(inp, k), "bf16", "cuda")
+             for k in ("x", "W_attn", "b_attn", "W_proj", "b_proj", "dY")}
+        ga.gpt_attn_set_dropout(layer.h, p, seed)
+        layer.forward(d["x"], d["W_attn"], d["b_attn"], d["W_proj"], d["b_proj"],
+                      save_for_backward=True)
+        g = {k: from_torch(v) for k, v in
+             layer.backward(d["x"], d["W_attn"], d["W_proj"], d["dY"]).items()}
+        torch.cuda.synchronize()
+        pf = float(np.float32(p))
+        r = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, H,
+                            want_inter=True, p=pf, seed=seed)
+        r["ym"] = oracle.forward_dropout(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
+                                         H, pf, seed, want_ym=True)["ym"]
+        sig = grad_gate.sigmas(dataclasses.replace(inp, dY=inp.dY / (1 - pf)), r)
+        for k in ("dx", "dW_attn", "db_attn", "dW_proj", "db_proj"):
+            grad_gate.check(k, g[k], r[k], sig[k])
+    layer.close()
