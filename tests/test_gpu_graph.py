@@ -75,3 +75,27 @@ def test_graph_decode_step_replays_match_eager():
 
     _replays_match(step, [yt], torch.cuda.Stream())
     layer.close()
+
+
+def test_graph_dropout_training_step_replays_match_eager():
+    """The training step with dropout on: the forward also stores the keep
+    bits that the backward reads; replays with the same seed reproduce the
+    eager outputs and gradients bit for bit."""
+    import torch
+    B, T, C, H = 2, 200, 256, 4
+    inp = make_inputs(B, T, C, H, bias=True, dtype="bf16", seed=47, with_dY=True)
+    t = device_inputs(inp)
+    layer = ga.Layer(C, H, B, T, "bf16")
+    ga.gpt_attn_set_dropout(layer.h, 0.1, 2024)
+    y = torch.empty_like(t["x"])
+    g = {k: torch.empty_like(t[src]) for k, src in
+         (("dx", "x"), ("dWa", "W_attn"), ("dba", "b_attn"), ("dWp", "W_proj"), ("dbp", "b_proj"))}
+
+    def step(s):
+        ga.gpt_attn_forward(layer.h, t["x"], t["W_attn"], t["b_attn"], t["W_proj"], t["b_proj"],
+                            H, y, stream=s, save_for_backward=True)
+        ga.gpt_attn_backward(layer.h, t["x"], t["W_attn"], t["W_proj"], t["dY"], g["dx"],
+                             g["dWa"], g["dba"], g["dWp"], g["dbp"], stream=s)
+
+    _replays_match(step, [y, *g.values()], torch.cuda.Stream())
+    layer.close()
