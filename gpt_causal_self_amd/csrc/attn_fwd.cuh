@@ -48,9 +48,11 @@ constexpr int kAttnBK = 64;   // keys per tile
 //    [key][d] tile, in the permuted key order of the probability registers
 //    (no register transposition);
 //  * the score scale folded into the exp2 argument with one FMA, and lazy
-//    rescaling: the running reference max only moves (rescaling l and the
-//    accumulators) when a tile's max exceeds it by more than 8 in log2 units,
-//    so probabilities stay <= 2^8 and most tiles skip the rescale.
+//    rescaling: the running reference (a whole number in log2 units, at or
+//    above the max that set it) only moves (rescaling l and the accumulators)
+//    when a tile's max exceeds it by more than 8, so unnormalised weights
+//    stay below 2^8 and most tiles skip the rescale.  Each weight is rounded
+//    to bf16 as the P.V operand; the row sum adds the unrounded weights.
 // Chunk swizzle of a key row.  LDS has 64 four-byte banks (256 bytes per
 // bank line), so a 128-byte row (HS = 64) shares its bank line with one
 // neighbour and a 64-byte row (HS = 32) with three.  The swizzle keeps both
@@ -249,14 +251,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
       for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sc[kt][r]);
     smax = fmaxf(smax, __shfl_xor(smax, 32));
     const float tmax = smax * scale_log2;
-    // ---- lazy rescale (wave-uniform branch)
+    // ---- lazy rescale (wave-uniform branch).  The reference is a whole
+    // number (log2 units), so every weight is the true softmax weight times a
+    // power of two: its bf16 rounding below does not depend on which tile
+    // last moved the reference.
     const bool need = tmax > m + kLazy;
-#ifdef GA_ATTN_EAGER_RESCALE
-    {
-#else
     if (__any(need)) {
-#endif
-      const float m_new = need ? tmax : m;
+      const float m_new = need ? __builtin_ceilf(tmax) : m;
       const float alpha = need ? __builtin_amdgcn_exp2f(m - m_new) : 1.f;
       m = m_new;
       l *= alpha;
