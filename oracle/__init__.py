@@ -119,7 +119,11 @@ def forward(x, W_attn, b_attn, W_proj, b_proj, n_head, *, want=("y",),
     "P" [B,H,T,T] (attention probabilities), "lse" [B,H,T].
     ``store_bf16`` may name "qkv" and/or "ym": those intermediates are then
     rounded to bfloat16 (nearest-even) where a bf16 path stores them; all
-    arithmetic stays fp64.  Returns a dict of float64 arrays."""
+    arithmetic stays fp64.  "P" forms the merged heads with the weights a
+    bf16 path feeds its P.V product: each unnormalised weight, taken
+    relative to a whole power of two, rounded to bfloat16, over the sum of
+    the unrounded weights ("P" and "lse" outputs stay the exact softmax).
+    Returns a dict of float64 arrays."""
     lib = lib or load()
     x = _f64(x)
     B, T, C = x.shape
@@ -141,14 +145,24 @@ def forward(x, W_attn, b_attn, W_proj, b_proj, n_head, *, want=("y",),
                             _ptr(W_proj), _ptr(b_proj), _ptr(out["y"]),
                             _ptr(out.get("qkv")), _ptr(out.get("ym")),
                             _ptr(out.get("P")), _ptr(out.get("lse")),
-                            (1 if "qkv" in store_bf16 else 0) | (2 if "ym" in store_bf16 else 0),
-                            int(nthreads or default_threads()))
+                            _fwd_bits(store_bf16), int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_forward failed (bad shape or out of memory)")
     return {k: v for k, v in out.items() if k in want}
 
 
-_STORE_BITS = {"qkv": 1, "ym": 2, "dym": 4, "dqkv": 8, "dyd": 16}
+_STORE_BITS = {"qkv": 1, "ym": 2, "dym": 4, "dqkv": 8, "dyd": 16, "P": 32, "Pb": 64,
+               "Do": 128, "dS": 256, "z32": 512}
+
+
+def _fwd_bits(store_bf16):
+    """Forward rounding options: "qkv", "ym", "P" (see ``forward``) and, for
+    ``forward_dropout``, "z32" (the keep factor 1/(1-p) held as the nearest
+    float)."""
+    bad = set(store_bf16) - {"qkv", "ym", "P", "z32"}
+    if bad:
+        raise ValueError(f"unknown forward rounding option(s) {sorted(bad)}")
+    return sum(_STORE_BITS[k] for k in set(store_bf16))
 
 
 def backward(x, W_attn, b_attn, W_proj, b_proj, dY, n_head, *, want_inter=False,
@@ -160,7 +174,14 @@ def backward(x, W_attn, b_attn, W_proj, b_proj, dY, n_head, *, want_inter=False,
     ``store_bf16`` may name "qkv", "ym", "dym", "dqkv" (and, with dropout,
     "dyd": the masked, rescaled upstream gradient of the c_proj output):
     those stored tensors are rounded to bfloat16 and the gradients are the
-    exact chain rule through the rounded values.  ``p`` > 0: gradient of the
+    exact chain rule through the rounded values.  "P" forms the forward's
+    merged heads as ``forward`` does; "Pb" sums the value gradient over
+    bf16(p_ij z_ij), the operand a bf16 path feeds that product (the softmax
+    gradient itself uses the exact p); "Do" forms the softmax gradient's row
+    term sum_j p_ij dp_ij as dO_i . o_i from the merged heads the forward
+    stored; "dS" rounds each dS_ij to bfloat16 before the query and key
+    gradients; with dropout "z32" holds the keep factor 1/(1-p) as the
+    nearest float.  ``p`` > 0: gradient of the
     forward with dropout rate p and generator ``seed`` (forward_dropout)."""
     lib = lib or load()
     x = _f64(x)
@@ -208,7 +229,7 @@ def layernorm(x, w, b, *, nthreads=None, lib=None):
 def block_attn_forward(x, ln_w, ln_b, W_attn, b_attn, W_proj, b_proj, n_head, *,
                        want_ln=False, store_bf16=(), nthreads=None, lib=None):
     """Attention half of a Pre-LN block: x + layer(ln_1(x)), fp64.
-    ``store_bf16`` may name "ln", "qkv", "ym"."""
+    ``store_bf16`` may name "ln", "qkv", "ym", "P"."""
     lib = lib or load()
     x = _f64(x)
     B, T, C = x.shape
@@ -216,8 +237,7 @@ def block_attn_forward(x, ln_w, ln_b, W_attn, b_attn, W_proj, b_proj, n_head, *,
         _f64, (ln_w, ln_b, W_attn, b_attn, W_proj, b_proj))
     out = np.empty((B, T, C))
     ln = np.empty((B, T, C)) if want_ln else None
-    bits = ((1 if "qkv" in store_bf16 else 0) | (2 if "ym" in store_bf16 else 0) |
-            (16 if "ln" in store_bf16 else 0))
+    bits = _fwd_bits(set(store_bf16) - {"ln"}) | (16 if "ln" in store_bf16 else 0)
     rc = lib.oracle_block_attn_forward(B, T, C, int(n_head), _ptr(x), _ptr(ln_w), _ptr(ln_b),
                                        _ptr(W_attn), _ptr(b_attn), _ptr(W_proj), _ptr(b_proj),
                                        _ptr(out), _ptr(ln), bits,
@@ -278,7 +298,8 @@ def forward_dropout(x, W_attn, b_attn, W_proj, b_proj, n_head, p, seed, *, want_
                     store_bf16=(), nthreads=None, lib=None):
     """Forward with dropout rate p on the attention weights and on the c_proj
     output (Philox masks keyed by ``seed``); fp64.  ``store_bf16`` may name
-    "qkv" and "ym"."""
+    "qkv", "ym" and "P" (as in ``forward``) and "z32" (the keep factor held
+    as the nearest float)."""
     lib = lib or load()
     x = _f64(x)
     B, T, C = x.shape
@@ -287,8 +308,7 @@ def forward_dropout(x, W_attn, b_attn, W_proj, b_proj, n_head, p, seed, *, want_
     ym = np.empty((B, T, C)) if want_ym else None
     rc = lib.oracle_forward_dropout(
         B, T, C, int(n_head), _ptr(x), _ptr(W_attn), _ptr(b_attn), _ptr(W_proj), _ptr(b_proj),
-        float(p), int(seed), _ptr(y), _ptr(ym),
-        (1 if "qkv" in store_bf16 else 0) | (2 if "ym" in store_bf16 else 0),
+        float(p), int(seed), _ptr(y), _ptr(ym), _fwd_bits(store_bf16),
         int(nthreads or default_threads()))
     if rc != 0:
         raise ValueError("oracle_forward_dropout failed (bad arguments or out of memory)")

@@ -171,13 +171,13 @@ typedef struct {
   double *ym;        /* [B*T][C] merged heads */
   double *P;         /* optional [B][H][T][T] */
   double *lse;       /* optional [B][H][T] */
+  int round_p;       /* weights of o = sum_j p_j v_j as the bf16 path rounds them */
 } attn_ctx;
 
-/* Probabilities of query row i of head (b, h): p[j] for j <= i.
- * s_j = (q_i . k_j) / sqrt(hs); two-pass softmax.  Returns the row's
- * log-sum-exp log(sum_j exp(s_j)). */
-static double prob_row(const double *qkv, int T, int C, int H, int b, int h,
-                       int i, double *p) {
+/* Scores of query row i of head (b, h): s[j] = (q_i . k_j) / sqrt(hs) for
+ * j <= i.  Returns their maximum. */
+static double score_row(const double *qkv, int T, int C, int H, int b, int h,
+                        int i, double *s) {
   const int hs = C / H;
   const size_t ld = (size_t)3 * C;
   const double scale = 1.0 / sqrt((double)hs);
@@ -187,9 +187,18 @@ static double prob_row(const double *qkv, int T, int C, int H, int b, int h,
     const double *k = qkv + ((size_t)b * T + j) * ld + C + (size_t)h * hs;
     double dot = 0.0;
     for (int d = 0; d < hs; ++d) dot += q[d] * k[d];
-    p[j] = dot * scale;
-    if (p[j] > m) m = p[j];
+    s[j] = dot * scale;
+    if (s[j] > m) m = s[j];
   }
+  return m;
+}
+
+/* Probabilities of query row i of head (b, h): p[j] for j <= i.
+ * s_j = (q_i . k_j) / sqrt(hs); two-pass softmax.  Returns the row's
+ * log-sum-exp log(sum_j exp(s_j)). */
+static double prob_row(const double *qkv, int T, int C, int H, int b, int h,
+                       int i, double *p) {
+  const double m = score_row(qkv, T, C, H, b, h, i, p);
   double Z = 0.0;
   for (int j = 0; j <= i; ++j) {
     p[j] = exp(p[j] - m);
@@ -199,19 +208,46 @@ static double prob_row(const double *qkv, int T, int C, int H, int b, int h,
   return m + log(Z);
 }
 
+/* The weights with which a bf16 path forms o_i = sum_j p_ij v_j when it
+ * feeds each weight to its bf16 matrix product as a bf16 value and
+ * normalises by the sum of the unrounded weights.  The unnormalised weight
+ * is taken relative to a whole power of two, u_j = 2^(t_j - M) with
+ * t_j = s_j log2(e) and M = ceil(max_j t_j), so that its rounding does not
+ * depend on which reference the path used: rounding to 8 significant bits
+ * commutes with scaling by any power of two.  w[j] = bf16(u_j) / sum_j' u_j'.
+ * s: the row's scaled scores (j < n); w may alias s. */
+static void pv_weights_bf16(const double *s, int n, double *w) {
+  const double log2e = 1.0 / log(2.0);
+  double tmax = -INFINITY;
+  for (int j = 0; j < n; ++j)
+    if (s[j] * log2e > tmax) tmax = s[j] * log2e;
+  const double M = ceil(tmax);
+  double U = 0.0;
+  for (int j = 0; j < n; ++j) {
+    w[j] = exp2(s[j] * log2e - M);
+    U += w[j];
+  }
+  for (int j = 0; j < n; ++j) w[j] = round_bf16(w[j]) / U;
+}
+
 static void attn_head(void *vctx, long item, double *p) {
   const attn_ctx *c = (const attn_ctx *)vctx;
   const int b = (int)(item / c->H), h = (int)(item % c->H);
   const int T = c->T, C = c->C, H = c->H, hs = C / H;
   const size_t ld = (size_t)3 * C;
+  double *wp = c->round_p ? p + T : p; /* weights of the value rows */
   for (int i = 0; i < T; ++i) {
     const double l = prob_row(c->qkv, T, C, H, b, h, i, p);
+    if (c->round_p) {
+      score_row(c->qkv, T, C, H, b, h, i, wp);
+      pv_weights_bf16(wp, i + 1, wp);
+    }
     double *o = c->ym + ((size_t)b * T + i) * C + (size_t)h * hs;
     for (int d = 0; d < hs; ++d) o[d] = 0.0;
     for (int j = 0; j <= i; ++j) {
       const double *v =
           c->qkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;
-      for (int d = 0; d < hs; ++d) o[d] += p[j] * v[d];
+      for (int d = 0; d < hs; ++d) o[d] += wp[j] * v[d];
     }
     if (c->P) {
       double *row = c->P + (((size_t)b * H + h) * T + i) * T;
@@ -228,7 +264,9 @@ static void attn_head(void *vctx, long item, double *p) {
  * b_proj [C] or NULL.  Outputs: y [B][T][C] (required); qkv [B][T][3C],
  * ym [B][T][C], P [B][H][T][T], lse [B][H][T] (each optional, NULL = not
  * wanted).  store_bf16: bit 0 rounds qkv to bfloat16 after step 1, bit 1
- * rounds the merged heads after step 7 (0 = exact fp64 throughout).
+ * rounds the merged heads after step 7, bit 5 (value 32) forms step 6 with
+ * the weights a bf16 path feeds its P.V product (pv_weights_bf16); P and
+ * lse stay the exact softmax (0 = exact fp64 throughout).
  * Returns 0, or -1 on bad arguments / allocation failure. */
 int oracle_forward(int B, int T, int C, int H, const double *x,
                    const double *W_attn, const double *b_attn,
@@ -246,8 +284,8 @@ int oracle_forward(int B, int T, int C, int H, const double *x,
   if (linear((int)M, C, 3 * C, x, W_attn, b_attn, qkv, nthreads)) goto done;
   if (store_bf16 & 1) round_all(qkv, (size_t)M * 3 * C);
   {
-    attn_ctx a = {B, T, C, H, qkv, ym, P_out, lse_out};
-    if (parallel_for((long)B * H, nthreads, attn_head, &a, (size_t)T)) goto done;
+    attn_ctx a = {B, T, C, H, qkv, ym, P_out, lse_out, (store_bf16 & 32) != 0};
+    if (parallel_for((long)B * H, nthreads, attn_head, &a, (size_t)2 * T)) goto done;
   }
   if (store_bf16 & 2) round_all(ym, (size_t)M * C);
   if (linear((int)M, C, C, ym, W_proj, b_proj, y, nthreads)) goto done;
@@ -306,14 +344,27 @@ static void dgrad_row(void *vctx, long m, double *scratch) {
   }
 }
 
+/* Factor of a kept element under dropout rate p, 1 / (1 - p); with
+ * scale32 the float nearest to it, the factor a path that computes in single
+ * precision multiplies by. */
+static double keep_scale_of(double p, int scale32) {
+  const double s = 1.0 / (1.0 - p);
+  return scale32 ? (double)(float)s : s;
+}
+
 /* Attention backward for one (b, h): from dym (gradient of the merged
  * heads) to the q, k, v column blocks of dqkv. */
 typedef struct {
   int B, T, C, H;
   const double *qkv, *dym;
+  const double *ym; /* merged heads as stored by the forward */
   double *dqkv;
   double p;      /* dropout rate of the attention weights (0: none) */
   uint64_t seed;
+  int round_pb;  /* dv_j sums bf16(p_ij z_ij) dO_i, as a bf16 path's product */
+  int row_from_o; /* row term as dO_i . o_i over the stored merged heads */
+  int round_ds;   /* dq, dk sum bf16(ds_ij), as a bf16 path's products */
+  int scale32;    /* keep factor held in single precision */
 } attn_bwd_ctx;
 
 int oracle_dropout_keep_attn(int b, int h, int H, int i, int j, uint64_t seed, uint32_t thresh);
@@ -329,7 +380,7 @@ static void attn_bwd_head(void *vctx, long item, double *scratch) {
   double *dp = scratch + T;  /* [T] dL/dp_ij               */
   /* dropout: weight p_ij enters o_i as p_ij z_ij with z_ij = 1/(1-p) if
    * kept, 0 if dropped (z = 1 without dropout) */
-  const double keep_scale = c->p > 0.0 ? 1.0 / (1.0 - c->p) : 1.0;
+  const double keep_scale = c->p > 0.0 ? keep_scale_of(c->p, c->scale32) : 1.0;
   const uint32_t thresh = c->p > 0.0 ? oracle_dropout_threshold(c->p) : 0u;
   /* zero this head's dq, dk, dv columns */
   for (int t = 0; t < T; ++t) {
@@ -348,20 +399,30 @@ static void attn_bwd_head(void *vctx, long item, double *scratch) {
       const double z =
           (c->p > 0.0 && !oracle_dropout_keep_attn(b, h, H, i, j, c->seed, thresh)) ? 0.0
                                                                                     : keep_scale;
+      double pv = p[j] * z;
+      if (c->round_pb) pv = round_bf16(pv);
       double s = 0.0;
       for (int d = 0; d < hs; ++d) {
         s += dO[d] * vj[d];
-        dvj[d] += p[j] * z * dO[d];
+        dvj[d] += pv * dO[d];
       }
       dp[j] = s * z;
       rowdot += p[j] * dp[j];
     }
     /* softmax Jacobian: ds_ij = p_ij (dp_ij - sum_j' p_ij' dp_ij');
      * scores s_ij = scale q_i . k_j  =>  dq_i += scale ds_ij k_j,
-     * dk_j += scale ds_ij q_i */
+     * dk_j += scale ds_ij q_i.  The row term equals dO_i . o_i (o_i is
+     * sum_j p_ij z_ij v_j); row_from_o forms it that way from the stored
+     * merged heads, as a path that keeps only those does. */
+    if (c->row_from_o) {
+      const double *oi = c->ym + ((size_t)b * T + i) * C + (size_t)h * hs;
+      rowdot = 0.0;
+      for (int d = 0; d < hs; ++d) rowdot += dO[d] * oi[d];
+    }
     double *dqi = c->dqkv + ((size_t)b * T + i) * ld + (size_t)h * hs;
     for (int j = 0; j <= i; ++j) {
-      const double ds = p[j] * (dp[j] - rowdot);
+      double ds = p[j] * (dp[j] - rowdot);
+      if (c->round_ds) ds = round_bf16(ds);
       const double *kj = c->qkv + ((size_t)b * T + j) * ld + C + (size_t)h * hs;
       double *dkj = c->dqkv + ((size_t)b * T + j) * ld + C + (size_t)h * hs;
       for (int d = 0; d < hs; ++d) {
@@ -380,7 +441,15 @@ static void attn_bwd_head(void *vctx, long item, double *scratch) {
  * store_bf16 rounds stored tensors to bfloat16 where a bf16 path stores
  * them: bit 0 qkv and bit 1 the merged heads (as in oracle_forward), bit 2
  * the gradient of the merged heads, bit 3 the gradient of qkv; every
- * gradient is then the exact chain rule through those stored values. */
+ * gradient is then the exact chain rule through those stored values.  Bit 5
+ * (32) forms the forward's merged heads with the bf16 path's P.V weights
+ * (as in oracle_forward); bit 6 (64) sums dv_j over bf16(p_ij z_ij), the
+ * value-gradient operand a bf16 path feeds its matrix product (the softmax
+ * gradient keeps the exact p); bit 7 (128) forms the softmax gradient's row
+ * term as dO_i . o_i from the merged heads the forward stored (rounded when
+ * bit 1 is set); bit 8 (256) rounds each ds_ij to bfloat16 before the query
+ * and key gradients, as a bf16 path's operands; bit 9 (512) holds the
+ * dropout keep factor 1/(1-p) in single precision. */
 static int forward_dropout_impl(int B, int T, int C, int H, const double *x,
                                 const double *W_attn, const double *b_attn,
                                 const double *W_proj, const double *b_proj, double p,
@@ -407,12 +476,12 @@ static int backward_impl(int B, int T, int C, int H, const double *x, const doub
   if (!qkv || !ym || !y || !dyd || !dym || !dqkv) goto done;
   if (p_drop > 0.0) {
     if (M > 0 && forward_dropout_impl(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, p_drop,
-                                      seed, y, qkv, ym, store_bf16 & 3, nthreads))
+                                      seed, y, qkv, ym, store_bf16 & 547, nthreads))
       goto done;
     /* resid_dropout: y = drop(ym . W_proj + b_proj)  =>  the c_proj
      * gradients see dY z with z = 1/(1-p) (kept) or 0 (dropped) */
     const uint32_t thresh = oracle_dropout_threshold(p_drop);
-    const double ks = 1.0 / (1.0 - p_drop);
+    const double ks = keep_scale_of(p_drop, (store_bf16 & 512) != 0);
     for (long m = 0; m < M; ++m)
       for (int n = 0; n < C; ++n)
         dyd[(size_t)m * C + n] = oracle_dropout_keep_resid(m, n, seed, thresh)
@@ -421,7 +490,7 @@ static int backward_impl(int B, int T, int C, int H, const double *x, const doub
     if (store_bf16 & 16) round_all(dyd, (size_t)M * C);
   } else {
     if (oracle_forward(B, T, C, H, x, W_attn, b_attn, W_proj, b_proj, y, qkv, ym,
-                       NULL, NULL, store_bf16 & 3, nthreads))
+                       NULL, NULL, store_bf16 & 35, nthreads))
       goto done;
     memcpy(dyd, dY, (size_t)M * C * sizeof(double));
   }
@@ -436,7 +505,10 @@ static int backward_impl(int B, int T, int C, int H, const double *x, const doub
   if (store_bf16 & 4) round_all(dym, (size_t)M * C);
   /* attention core */
   {
-    attn_bwd_ctx a = {B, T, C, H, qkv, dym, dqkv, p_drop, seed};
+    attn_bwd_ctx a = {B,     T,     C,          H,
+                      qkv,   dym,   ym,         dqkv,
+                      p_drop, seed, (store_bf16 & 64) != 0, (store_bf16 & 128) != 0,
+                      (store_bf16 & 256) != 0, (store_bf16 & 512) != 0};
     if (parallel_for((long)B * H, nthreads, attn_bwd_head, &a, (size_t)2 * T + 2))
       goto done;
   }
@@ -521,7 +593,7 @@ int oracle_layernorm(int M, int C, const double *x, const double *w, const doubl
 }
 
 /* Attention half of a Pre-LN block: out = x + layer(ln_1(x)).
- * store_bf16 bits 0/1 as in oracle_forward; bit 4 rounds the LayerNorm
+ * store_bf16 bits 0/1/5 as in oracle_forward; bit 4 rounds the LayerNorm
  * output (the layer's input) to bfloat16.  ln_out [B][T][C] optional. */
 int oracle_block_attn_forward(int B, int T, int C, int H, const double *x,
                               const double *ln_w, const double *ln_b,
@@ -538,7 +610,7 @@ int oracle_block_attn_forward(int B, int T, int C, int H, const double *x,
   if (oracle_layernorm((int)M, C, x, ln_w, ln_b, ln, nthreads)) goto done;
   if (store_bf16 & 16) round_all(ln, (size_t)M * C);
   if (oracle_forward(B, T, C, H, ln, W_attn, b_attn, W_proj, b_proj, y, NULL, NULL,
-                     NULL, NULL, store_bf16 & 3, nthreads))
+                     NULL, NULL, store_bf16 & 35, nthreads))
     goto done;
   for (size_t i = 0; i < (size_t)M * C; ++i) out[i] = x[i] + y[i];
   rc = 0;
@@ -639,6 +711,8 @@ typedef struct {
   double p;
   uint64_t seed;
   uint32_t thresh;
+  int round_p; /* as attn_ctx.round_p */
+  int scale32; /* keep factor held in single precision */
 } drop_attn_ctx;
 
 /* Head (b, h) with dropout on the softmax weights: the row is normalised
@@ -649,14 +723,19 @@ static void drop_attn_head(void *vctx, long item, double *p) {
   const int b = (int)(item / c->H), h = (int)(item % c->H);
   const int T = c->T, C = c->C, H = c->H, hs = C / H;
   const size_t ld = (size_t)3 * C;
-  const double keep_scale = 1.0 / (1.0 - c->p);
+  const double keep_scale = keep_scale_of(c->p, c->scale32);
+  double *wp = c->round_p ? p + T : p; /* weights of the value rows */
   for (int i = 0; i < T; ++i) {
     prob_row(c->qkv, T, C, H, b, h, i, p);
+    if (c->round_p) {
+      score_row(c->qkv, T, C, H, b, h, i, wp);
+      pv_weights_bf16(wp, i + 1, wp);
+    }
     double *o = c->ym + ((size_t)b * T + i) * C + (size_t)h * hs;
     for (int d = 0; d < hs; ++d) o[d] = 0.0;
     for (int j = 0; j <= i; ++j) {
       if (!oracle_dropout_keep_attn(b, h, H, i, j, c->seed, c->thresh)) continue;
-      const double w = p[j] * keep_scale;
+      const double w = wp[j] * keep_scale;
       const double *v = c->qkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;
       for (int d = 0; d < hs; ++d) o[d] += w * v[d];
     }
@@ -666,7 +745,8 @@ static void drop_attn_head(void *vctx, long item, double *p) {
 /* Forward with dropout rate p (0 <= p < 1) on the attention weights and on
  * the c_proj output, masks from Philox keyed by `seed` as above.  Arguments
  * otherwise as oracle_forward (ym_out optional; store_bf16 bits 0 / 1 round
- * qkv / merged heads).  p = 0 keeps everything (same result as
+ * qkv / merged heads, bit 5 takes the bf16 path's P.V weights, bit 9 (512)
+ * holds the keep factor 1/(1-p) in single precision).  p = 0 keeps everything (same result as
  * oracle_forward). */
 static int forward_dropout_impl(int B, int T, int C, int H, const double *x,
                                 const double *W_attn, const double *b_attn,
@@ -678,12 +758,14 @@ static int forward_dropout_impl(int B, int T, int C, int H, const double *x,
   if (linear((int)M, C, 3 * C, x, W_attn, b_attn, qkv, nthreads)) return -1;
   if (store_bf16 & 1) round_all(qkv, (size_t)M * 3 * C);
   {
-    drop_attn_ctx a = {B, T, C, H, qkv, ym, p, seed, thresh};
-    if (parallel_for((long)B * H, nthreads, drop_attn_head, &a, (size_t)T)) return -1;
+    drop_attn_ctx a = {B,      T,      C,                       H,
+                       qkv,    ym,     p,                       seed,
+                       thresh, (store_bf16 & 32) != 0, (store_bf16 & 512) != 0};
+    if (parallel_for((long)B * H, nthreads, drop_attn_head, &a, (size_t)2 * T)) return -1;
   }
   if (store_bf16 & 2) round_all(ym, (size_t)M * C);
   if (linear((int)M, C, C, ym, W_proj, b_proj, y, nthreads)) return -1;
-  const double keep_scale = 1.0 / (1.0 - p);
+  const double keep_scale = keep_scale_of(p, (store_bf16 & 512) != 0);
   for (long m = 0; m < M; ++m)
     for (int n = 0; n < C; ++n)
       y[(size_t)m * C + n] = oracle_dropout_keep_resid(m, n, seed, thresh)

@@ -3,10 +3,10 @@
 The oracle's gradients are the exact chain rule through the layer (pinned on
 the CPU by finite differences and torch autograd).  The GPU returns them in
 the parameter dtype with fp32 accumulation.  fp32 results are held to a
-maximum absolute error of 1e-4; bf16 results to the gradient gate derived in
-``grad_gate.py`` (the stated bf16 tolerance widened by six standard
-deviations of the bf16 rounding noise of each contraction) plus a normwise
-gate of 1e-2."""
+maximum absolute error of 1e-4.  bf16 results are held to the stated
+tolerance |g - r| <= 2e-2 + 1e-2 |r| elementwise against the oracle that
+applies the bf16 path's roundings (``grad_gate.py``), and to a normwise
+error of at most 1e-2 against the exact oracle."""
 from __future__ import annotations
 
 import numpy as np
@@ -44,23 +44,18 @@ def gpu_train_step(inp, layer=None):
 
 def check_grads(inp):
     g = gpu_train_step(inp)
-    r = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY,
-                        inp.n_head, want_inter=True)
     if inp.dtype == "bf16":
-        r["ym"] = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
-                                 inp.n_head, want=("ym",))["ym"]
-        sig = grad_gate.sigmas(inp, r)
+        return grad_gate.check_all(g, inp)
+    r = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY,
+                        inp.n_head)
     errs = {}
     for k in GRADS:
         if k not in r:
             assert k not in g
             continue
-        if inp.dtype == "f32":
-            err = np.abs(g[k] - r[k]).max()
-            assert err <= 1e-4, (k, err)
-            errs[k] = err
-        else:
-            errs[k] = grad_gate.check(k, g[k], r[k], sig[k])
+        err = np.abs(g[k] - r[k]).max()
+        assert err <= 1e-4, (k, err)
+        errs[k] = err
     return errs
 
 
@@ -85,7 +80,10 @@ def test_backward_small_shapes(B, T, C, H, bias, dtype):
 def test_backward_training_step_workload_full():
     """The GPT-2 124M training step at its full shape (B12 T1024 C768 H12):
     every gradient against the full fp64 oracle backward."""
-    check_grads(workload_inputs(5))
+    stats = check_grads(workload_inputs(5))
+    for k, (ratio, rel) in stats.items():
+        print(f"training step {k}: max err / stated bound {ratio:.3f}, "
+              f"normwise vs exact {rel:.2e}", flush=True)
 
 
 def test_backward_deterministic():

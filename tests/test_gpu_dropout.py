@@ -12,8 +12,6 @@ from __future__ import annotations
 import numpy as np
 import pytest
 
-import dataclasses
-
 import grad_gate
 import oracle
 from gpt_causal_self_amd import gpt_attn as ga
@@ -143,9 +141,9 @@ def test_dropout_errors():
 @pytest.mark.parametrize("B,T,C,H,p,seed", [(2, 70, 256, 4, 0.1, 31), (1, 129, 128, 4, 0.5, 32),
                                             (2, 1024, 768, 12, 0.1, 33)])
 def test_dropout_backward(B, T, C, H, p, seed):
-    """Gradients of a dropout forward against the oracle's exact gradient
-    through the same masks, with the bf16 gradient gate; its rounding-noise
-    sigmas use |dY| / (1 - p), a bound on the masked upstream gradient."""
+    """Gradients of a dropout forward against the oracle's gradient through
+    the same masks: the stated tolerance elementwise against the oracle with
+    the bf16 path's roundings, normwise 1e-2 against the exact one."""
     import torch
     inp = make_inputs(B, T, C, H, dtype="bf16", seed=T + seed, with_dY=True)
     layer = ga.Layer(C, H, B, T, "bf16")
@@ -158,15 +156,7 @@ def test_dropout_backward(B, T, C, H, p, seed):
          layer.backward(d["x"], d["W_attn"], d["W_proj"], d["dY"]).items()}
     torch.cuda.synchronize()
     layer.close()
-    pf = float(np.float32(p))
-    r = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, H,
-                        want_inter=True, p=pf, seed=seed)
-    r["ym"] = oracle.forward_dropout(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, H,
-                                     pf, seed, want_ym=True)["ym"]
-    bound_inp = dataclasses.replace(inp, dY=inp.dY / (1 - pf))
-    sig = grad_gate.sigmas(bound_inp, r)
-    for k in ("dx", "dW_attn", "db_attn", "dW_proj", "db_proj"):
-        grad_gate.check(k, g[k], r[k], sig[k])
+    grad_gate.check_all(g, inp, p=float(np.float32(p)), seed=seed)
 
 
 @pytest.mark.parametrize("C,H", [(256, 4), (128, 4)])
@@ -188,12 +178,5 @@ def test_dropout_backward_below_the_handle_maxima(C, H):
         g = {k: from_torch(v) for k, v in
              layer.backward(d["x"], d["W_attn"], d["W_proj"], d["dY"]).items()}
         torch.cuda.synchronize()
-        pf = float(np.float32(p))
-        r = oracle.backward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, H,
-                            want_inter=True, p=pf, seed=seed)
-        r["ym"] = oracle.forward_dropout(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj,
-                                         H, pf, seed, want_ym=True)["ym"]
-        sig = grad_gate.sigmas(dataclasses.replace(inp, dY=inp.dY / (1 - pf)), r)
-        for k in ("dx", "dW_attn", "db_attn", "dW_proj", "db_proj"):
-            grad_gate.check(k, g[k], r[k], sig[k])
+        grad_gate.check_all(g, inp, p=float(np.float32(p)), seed=seed)
     layer.close()

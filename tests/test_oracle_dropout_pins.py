@@ -133,3 +133,30 @@ def test_backward_with_dropout_matches_finite_differences():
             fd = (lp - lm) / (2 * eps)
             an = g[gk].reshape(-1)[idx]
             assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (k, idx, fd, an)
+
+
+def check_single_precision_keep_factor(lib=None):
+    """"z32" holds 1/(1-p) as the nearest float.  At p = float32(0.2),
+    1/(1-p) = 1.2500000047 whose nearest float is exactly 1.25, so with the
+    stored masked gradient ("dyd") db_proj is the column sum of
+    bf16(keep * dY * 1.25); at p = 0.5 the factor 2 is exact either way."""
+    from test_oracle_pins import _bits_rne_bf16
+    B, T, C, H = 1, 9, 16, 2
+    inp = make_inputs(B, T, C, H, dtype="bf16", seed=53, w_std=0.3, with_dY=True)
+    args = (inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, H)
+    p = float(np.float32(0.2))
+    r = oracle.backward(*args, p=p, seed=5, store_bf16=("dyd", "z32"), lib=lib)
+    keep = np.array([[oracle.dropout_keep_resid(m, n, p, 5, lib=lib) for n in range(C)]
+                     for m in range(B * T)], dtype=float)
+    dyd = _bits_rne_bf16(keep * inp.dY.reshape(-1, C).astype(np.float64) * 1.25)
+    np.testing.assert_allclose(r["db_proj"], dyd.sum(0), rtol=1e-13, atol=1e-13)
+    r64 = oracle.backward(*args, p=p, seed=5, store_bf16=("dyd",), lib=lib)
+    assert not np.array_equal(r64["db_proj"], r["db_proj"])
+    a = oracle.backward(*args, p=0.5, seed=5, store_bf16=("dyd", "z32"), lib=lib)
+    b = oracle.backward(*args, p=0.5, seed=5, store_bf16=("dyd",), lib=lib)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_single_precision_keep_factor():
+    check_single_precision_keep_factor()

@@ -47,9 +47,9 @@ MUTANTS = [
      [("row[n] += a * w[n];",
        "row[n] += a * (c->K == c->N ? c->W[(size_t)n * c->N + k] : w[n]);", 0)]),
     ("softmax grad without row term",
-     [("const double ds = p[j] * (dp[j] - rowdot);", "const double ds = p[j] * dp[j];", 0)]),
+     [("double ds = p[j] * (dp[j] - rowdot);", "double ds = p[j] * dp[j];", 0)]),
     ("key grad sign", [("dkj[d] += scale * ds * qi[d];", "dkj[d] -= scale * ds * qi[d];", 0)]),
-    ("value grad wrong operand", [("dvj[d] += p[j] * z * dO[d];", "dvj[d] += p[j] * z * qi[d];", 0)]),
+    ("value grad wrong operand", [("dvj[d] += pv * dO[d];", "dvj[d] += pv * qi[d];", 0)]),
     ("query grad without scale", [("dqi[d] += scale * ds * kj[d];", "dqi[d] += ds * kj[d];", 0)]),
     ("bias grad drops last row",
      [("db[n] += dout[(size_t)m * N + n];",
@@ -70,13 +70,23 @@ MUTANTS = [
     ("mlp skips gelu", [("h[i] = gelu(h[i]);", "h[i] = h[i];", 0)]),
     ("philox multiplier", [("(uint64_t)0xD2511F53u * x0", "(uint64_t)0xD2511F57u * x0", 0)]),
     ("philox key schedule", [("k0 += 0x9E3779B9u;", "k0 += 0x9E3779B1u;", 0)]),
-    ("dropout weights not rescaled", [("const double w = p[j] * keep_scale;",
-                                       "const double w = p[j];", 0)]),
+    ("dropout weights not rescaled", [("const double w = wp[j] * keep_scale;",
+                                       "const double w = wp[j];", 0)]),
     ("residual dropout not rescaled", [("? y[(size_t)m * C + n] * keep_scale",
                                         "? y[(size_t)m * C + n]", 0)]),
     ("dropout word index", [("return w[c0 & 3] >= thresh;", "return w[0] >= thresh;", 0)]),
-    ("dropout backward: value grad unmasked", [("dvj[d] += p[j] * z * dO[d];",
-                                                "dvj[d] += p[j] * dO[d];", 0)]),
+    ("dropout backward: value grad unmasked", [("double pv = p[j] * z;",
+                                                "double pv = p[j];", 0)]),
+    ("P.V weights relative to the exact max", [("const double M = ceil(tmax);",
+                                                "const double M = tmax;", 0)]),
+    ("P.V weights over the rounded sum", [("U += w[j];", "U += round_bf16(w[j]);", 0)]),
+    ("P.V weights not rounded", [("w[j] = round_bf16(w[j]) / U;", "w[j] = w[j] / U;", 0)]),
+    ("value-gradient weights not rounded", [("if (c->round_pb) pv = round_bf16(pv);", "", 0)]),
+    ("dS not rounded", [("if (c->round_ds) ds = round_bf16(ds);", "", 0)]),
+    ("keep factor not held as a float", [("return scale32 ? (double)(float)s : s;", "return s;", 0)]),
+    ("row term from the merged heads uses the input",
+     [("for (int d = 0; d < hs; ++d) rowdot += dO[d] * oi[d];",
+       "for (int d = 0; d < hs; ++d) rowdot += dO[d] * qi[d];", 0)]),
     ("dropout backward: weight grad unmasked", [("dp[j] = s * z;", "dp[j] = s;", 0)]),
     ("dropout backward: output grad unmasked", [("? dY[(size_t)m * C + n] * ks", "? dY[(size_t)m * C + n]", 0)]),
     ("input grad with untransposed square weight",
@@ -177,6 +187,25 @@ def _pins(lib):
             fd = (vals[0] - vals[1]) / 2e-6
             if abs(fd - gd[gk].reshape(-1)[idx]) > 1e-6 * max(1.0, abs(fd)):
                 failed.append("dropout backward fd")
+    # the bf16 path's P.V and value-gradient weights: closed forms on a
+    # constant sequence
+    import test_oracle_pins as opin
+    try:
+        opin.check_pv_weights_constant_sequence(lib)
+    except AssertionError:
+        failed.append("P.V weights closed form")
+    try:
+        opin.check_value_grad_weights_constant_sequence(lib)
+    except AssertionError:
+        failed.append("value-gradient weights closed form")
+    try:
+        opin.check_row_term_and_ds_rounding(lib)
+    except AssertionError:
+        failed.append("row term and dS rounding")
+    try:
+        dpin.check_single_precision_keep_factor(lib)
+    except AssertionError:
+        failed.append("single-precision keep factor")
     # brute force forward, incl. P and the log-sum-exp
     for (B, T, C, H, bias) in ((2, 5, 8, 2, True), (2, 6, 16, 4, False)):
         inp = make_inputs(B, T, C, H, bias=bias, dtype="f32", seed=T, w_std=0.5,

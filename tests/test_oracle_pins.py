@@ -427,3 +427,165 @@ def test_backward_store_bf16_rounds_exactly_the_stored_tensors():
     r4 = oracle.backward(*args, want_inter=True, store_bf16=())
     for k in ex:
         assert np.array_equal(r4[k], ex[k])
+
+
+# --------------------------------- the bf16 path's P.V and dV weight rounding
+def _constant_sequence(B, T, C, H, seed, **kw):
+    """Inputs whose T positions all repeat position 0 of each sequence."""
+    import dataclasses
+    inp = make_inputs(B, T, C, H, dtype="f32", seed=seed, **kw)
+    x = np.repeat(inp.x[:, :1], T, axis=1)
+    dY = None if inp.dY is None else inp.dY
+    return dataclasses.replace(inp, x=x, dY=dY)
+
+
+def check_pv_weights_constant_sequence(lib=None):
+    """Every score of a row is s = q.k / sqrt(hs), so the weights the bf16
+    path feeds its P.V product are all u = 2^(t - ceil t) with t = s log2 e,
+    each rounded to bf16, over n u: o_i = v bf16(u) / u for every i."""
+    B, T, C, H = 2, 6, 16, 2
+    hs = C // H
+    inp = _constant_sequence(B, T, C, H, seed=41, w_std=0.6, b_attn_std=0.3)
+    r = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, H,
+                       want=("ym", "qkv"), store_bf16=("P",), lib=lib)
+    qkv = r["qkv"]
+    moved = 0
+    for b in range(B):
+        for h in range(H):
+            q = qkv[b, 0, h * hs:(h + 1) * hs]
+            k = qkv[b, 0, C + h * hs:C + (h + 1) * hs]
+            v = qkv[b, 0, 2 * C + h * hs:2 * C + (h + 1) * hs]
+            t = float(q @ k) / math.sqrt(hs) / math.log(2.0)
+            assert abs(t - round(t)) > 1e-6  # the reference is unambiguous
+            u = 2.0 ** (t - math.ceil(t))
+            ratio = float(_bits_rne_bf16(np.array([u]))[0]) / u
+            moved += ratio != 1.0
+            for i in range(T):
+                np.testing.assert_allclose(r["ym"][b, i, h * hs:(h + 1) * hs], v * ratio,
+                                           rtol=1e-12, atol=1e-15)
+    assert moved > 0
+
+
+def check_value_grad_weights_constant_sequence(lib=None):
+    """On a constant sequence p_ij = 1/(i+1) for j <= i, so with "Pb" the
+    value gradient is dv_j = sum_{i>=j} bf16(1/(i+1)) dO_i; the query and
+    key gradients are untouched."""
+    B, T, C, H = 1, 7, 16, 2
+    hs = C // H
+    inp = _constant_sequence(B, T, C, H, seed=43, w_std=0.5, with_dY=True)
+    args = (inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, H)
+    ex = oracle.backward(*args, want_inter=True, lib=lib)
+    r = oracle.backward(*args, want_inter=True, store_bf16=("Pb",), lib=lib)
+    w = _bits_rne_bf16(1.0 / np.arange(1, T + 1, dtype=np.float64))
+    dO = ex["dym"][0]
+    for h in range(H):
+        want = np.array([(w[j:, None] * dO[j:, h * hs:(h + 1) * hs]).sum(0) for j in range(T)])
+        np.testing.assert_allclose(r["dqkv"][0, :, 2 * C + h * hs:2 * C + (h + 1) * hs], want,
+                                   rtol=1e-12, atol=1e-14)
+    assert np.array_equal(r["dqkv"][..., :2 * C], ex["dqkv"][..., :2 * C])
+    assert not np.array_equal(r["dqkv"][..., 2 * C:], ex["dqkv"][..., 2 * C:])
+
+
+def test_pv_weights_constant_sequence():
+    check_pv_weights_constant_sequence()
+
+
+def test_value_grad_weights_constant_sequence():
+    check_value_grad_weights_constant_sequence()
+
+
+def test_pv_weights_error_bound_and_exact_outputs():
+    """Each P.V weight moves by at most 2^-8 of itself (one rounding to 8
+    significant bits), the normaliser is exact, so
+    |o_P - o| <= 2^-8 sum_j p_ij |v_j|; the
+    probabilities and log-sum-exp outputs are the exact softmax."""
+    B, T, C, H = 2, 33, 32, 2
+    hs = C // H
+    inp = make_inputs(B, T, C, H, dtype="f32", seed=45, w_std=0.4, b_attn_std=0.2)
+    ex = fwd(inp, want=("ym", "P", "lse", "qkv", "y"))
+    r = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, H,
+                       want=("ym", "P", "lse", "qkv"), store_bf16=("P",))
+    assert np.array_equal(r["P"], ex["P"]) and np.array_equal(r["lse"], ex["lse"])
+    assert np.array_equal(r["qkv"], ex["qkv"])
+    v = np.abs(ex["qkv"][..., 2 * C:]).reshape(B, T, H, hs).transpose(0, 2, 1, 3)
+    bound = (ex["P"] @ v).transpose(0, 2, 1, 3).reshape(B, T, C) * 2.0 ** -8
+    err = np.abs(r["ym"] - ex["ym"])
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-15)
+    assert err.max() > 0
+
+
+def test_value_grad_weights_error_bound():
+    """|dv_Pb - dv| <= 2^-8 sum_i p_ij |dO_i| (each weight rounded once)."""
+    B, T, C, H = 2, 21, 32, 4
+    hs = C // H
+    inp = make_inputs(B, T, C, H, dtype="f32", seed=47, w_std=0.4, with_dY=True)
+    args = (inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, H)
+    ex = oracle.backward(*args, want_inter=True)
+    r = oracle.backward(*args, want_inter=True, store_bf16=("Pb",))
+    P = fwd(inp, want=("P",))["P"]
+    dO = np.abs(ex["dym"]).reshape(B, T, H, hs).transpose(0, 2, 1, 3)
+    bound = (P.transpose(0, 1, 3, 2) @ dO).transpose(0, 2, 1, 3).reshape(B, T, C) * 2.0 ** -8
+    err = np.abs(r["dqkv"][..., 2 * C:] - ex["dqkv"][..., 2 * C:])
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-15)
+    assert err.max() > 0
+
+
+def _softmax_grad_pieces(inp, fwd_store, lib=None):
+    """Exact probabilities (pinned above), the oracle's merged heads and
+    merged-head gradient for the numpy reassembly of the attention backward."""
+    H = inp.n_head
+    f = oracle.forward(inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, H,
+                       want=("qkv", "ym", "P"), store_bf16=fwd_store, lib=lib)
+    args = (inp.x, inp.W_attn, inp.b_attn, inp.W_proj, inp.b_proj, inp.dY, H)
+    return f, args
+
+
+def _attn_grads_numpy(qkv, P, dO, o, H, row_from_o, round_ds):
+    """dq, dk, dv of one sequence by matrix products over the whole T x T
+    softmax (a different order of every sum than the oracle's loops)."""
+    T, C3 = qkv.shape
+    C = C3 // 3
+    hs = C // H
+    sc = 1.0 / math.sqrt(hs)
+    dq, dk, dv = (np.zeros((T, C)) for _ in range(3))
+    for h in range(H):
+        s = slice(h * hs, (h + 1) * hs)
+        q, k, v, g, p = qkv[:, s], qkv[:, C:][:, s], qkv[:, 2 * C:][:, s], dO[:, s], P[h]
+        dp = g @ v.T
+        D = (g * o[:, s]).sum(1) if row_from_o else (p * dp).sum(1)
+        ds = np.tril(p * (dp - D[:, None]))
+        if round_ds:
+            ds = _bits_rne_bf16(ds)
+        dq[:, s], dk[:, s], dv[:, s] = sc * ds @ k, sc * ds.T @ q, p.T @ g
+    return np.concatenate([dq, dk, dv], 1)
+
+
+def check_row_term_and_ds_rounding(lib=None):
+    """"Do" takes the softmax gradient's row term from the stored merged
+    heads, "dS" rounds dS to bf16 before the query and key gradients: both
+    against a numpy reassembly from the exact probabilities; and with
+    nothing rounded the row term from the merged heads is the Jacobian's
+    row term (sum_j p_ij dp_ij = dO_i . o_i)."""
+    B, T, C, H = 2, 11, 16, 2
+    inp = make_inputs(B, T, C, H, dtype="f32", seed=49, w_std=0.5, proj_std=0.5,
+                      with_dY=True)
+    f, args = _softmax_grad_pieces(inp, ("qkv", "ym"), lib)
+    ex = oracle.backward(*args, want_inter=True, lib=lib)
+    plain_o = oracle.backward(*args, want_inter=True, store_bf16=("Do",), lib=lib)
+    np.testing.assert_allclose(plain_o["dqkv"], ex["dqkv"], rtol=1e-10, atol=1e-13)
+    r = oracle.backward(*args, want_inter=True, store_bf16=("qkv", "ym", "Do", "dS"), lib=lib)
+    assert not np.allclose(r["dqkv"][..., :2 * C], ex["dqkv"][..., :2 * C], rtol=1e-6, atol=0)
+    for b in range(B):
+        want = _attn_grads_numpy(f["qkv"][b], f["P"][b], r["dym"][b], f["ym"][b], H,
+                                 row_from_o=True, round_ds=True)
+        np.testing.assert_allclose(r["dqkv"][b], want, rtol=1e-11, atol=1e-14)
+    rs = oracle.backward(*args, want_inter=True, store_bf16=("dS",), lib=lib)
+    fe, _ = _softmax_grad_pieces(inp, (), lib)
+    for b in range(B):
+        want = _attn_grads_numpy(fe["qkv"][b], fe["P"][b], ex["dym"][b], fe["ym"][b], H,
+                                 row_from_o=False, round_ds=True)
+        np.testing.assert_allclose(rs["dqkv"][b], want, rtol=1e-11, atol=1e-14)
+
+
+def test_row_term_and_ds_rounding():
+    check_row_term_and_ds_rounding()
