@@ -102,6 +102,19 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def cpu_model():
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(workload_index, n_seq, min_seconds=10.0):
     """The fp64 oracle, as it stands, on the first n_seq sequences of the
     same workload (sequences are independent, so throughput scales), run
@@ -121,7 +134,8 @@ def cpu_baseline(workload_index, n_seq, min_seconds=10.0):
     dt = (time.perf_counter() - t0) / runs
     B, T, C = inp.x.shape
     return {"value": layer_flops(B, T, C) / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "tokens_per_s": B * T / dt, "seconds_per_run": dt, "runs": runs,
+            "cpu_model": cpu_model(), "kind": "oracle", "tokens_per_s": B * T / dt,
+            "seconds_per_run": dt, "runs": runs,
             "sample": f"{n_seq} of 12 sequences (B={n_seq}, T=1024, C=768, H=12), fp64 "
                       f"forward on the same seeded inputs, mean of {runs} runs"}
 

@@ -42,12 +42,14 @@ namespace gpt_attn {
 constexpr int kDecMaxB = 16;     // rows of one decode call
 
 // Device-scope accesses of the fp32 partials that one block writes and the
-// last block of its group reads back.  Relaxed atomics at agent scope are
-// plain loads and stores marked coherent across the XCDs' L2 caches, so the
-// hand-off needs no whole-cache write-back or invalidation: each thread
-// waits until its partial stores have completed (vmcnt(0)) before the block
-// barrier that precedes the arrival count, and the last block reads the
-// partials with device-scope loads after the count.
+// last block of its group reads back: relaxed atomics at agent scope, i.e.
+// loads and stores coherent across the XCDs' L2 caches.  The ordering of the
+// hand-off comes from the arrival count (arrive_last): every thread's partial
+// stores precede the block barrier, the barrier precedes thread 0's
+// acquire-release increment at agent scope, and in the last block that
+// increment precedes the barrier after which its threads load the partials.
+// So each block's stores happen before the last block's loads (release
+// sequence on the counter, chained with the workgroup barriers).
 __device__ __forceinline__ void st_dev(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -66,7 +68,7 @@ __device__ __forceinline__ bool arrive_last(unsigned* c, unsigned n, int* flag) 
   wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     *flag = old == n - 1;
     if (old == n - 1) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
