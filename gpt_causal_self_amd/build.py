@@ -1,10 +1,11 @@
 """Build the HIP library ``libgpt_attn.so`` in-tree with hipcc for gfx950.
 
-Three translation units hold the C ABI and include the kernel headers:
+Four translation units hold the C ABI and include the kernel headers:
 ``csrc/gpt_attn.hip`` (the attention layer, include/gpt_attn.h),
 ``csrc/gpt_block.hip`` (LayerNorm, the Pre-LN half-block, the MLP;
-include/gpt_block.h) and ``csrc/gpt_decode.hip`` (one-token decode with a
-key/value cache; include/gpt_decode.h).  Packed-fp32 instructions are disabled for every kernel
+include/gpt_block.h), ``csrc/gpt_decode.hip`` (one-token decode with a
+key/value cache; include/gpt_decode.h) and ``csrc/gpt_noalloc.hip`` (the
+allocation-free forward with its static device scratch; include/gpt_attn.h).  Packed-fp32 instructions are disabled for every kernel
 (``-target-feature -packed-fp32-ops``); hipcc's host pass warns that it does
 not know that feature, which is harmless.
 """
@@ -17,7 +18,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", n) for n in ("gpt_attn.hip", "gpt_block.hip", "gpt_decode.hip")]
+SRCS = [os.path.join(HERE, "csrc", n)
+        for n in ("gpt_attn.hip", "gpt_block.hip", "gpt_decode.hip", "gpt_noalloc.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgpt_attn.so")
 ARCH = os.environ.get("GPT_ATTN_ARCH", "gfx950")

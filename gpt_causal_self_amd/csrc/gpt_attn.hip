@@ -21,7 +21,7 @@ const char* gpt_attn_strerror(int code) {
   switch (code) {
     case GPT_ATTN_OK: return "ok";
     case GPT_ATTN_ERR_INVALID_ARG: return "invalid argument (NULL pointer, non-positive size or unknown dtype)";
-    case GPT_ATTN_ERR_SHAPE: return "shape error (C % n_head != 0, n_head mismatch, or B/T above the handle's maximum)";
+    case GPT_ATTN_ERR_SHAPE: return "shape error (C % n_head != 0, n_head mismatch, B/T above the handle's maximum, or intermediates larger than the allocation-free forward's static scratch)";
     case GPT_ATTN_ERR_UNSUPPORTED: return "unsupported configuration (head size must be 32 or 64)";
     case GPT_ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case GPT_ATTN_ERR_OOM: return "device workspace allocation failed";

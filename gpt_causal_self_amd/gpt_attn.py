@@ -23,7 +23,7 @@ EXPORTED = ("gpt_attn_workspace_bytes", "gpt_attn_create", "gpt_attn_forward",
             "gpt_attn_debug_workspace", "gpt_attn_set_stage_events",
             "gpt_attn_debug_backward", "gpt_layernorm", "gpt_attn_block_forward",
             "gpt_mlp_forward", "gpt_attn_decode", "gpt_attn_export_kv",
-            "gpt_attn_set_dropout")
+            "gpt_attn_set_dropout", "gpt_attn_forward_noalloc")
 
 _lib = None
 
@@ -62,6 +62,7 @@ def lib():
         L.gpt_attn_decode.argtypes = [vp, vp, i, i, vp, vp, vp, vp, i, vp, vp, i, vp, vp]
         L.gpt_attn_export_kv.argtypes = [vp, vp, vp, i, vp]
         L.gpt_attn_set_dropout.argtypes = [vp, ctypes.c_float, ctypes.c_ulonglong]
+        L.gpt_attn_forward_noalloc.argtypes = [vp, i, i, i, i, vp, vp, vp, vp, vp, vp]
         for name in EXPORTED:
             if name != "gpt_attn_strerror":
                 getattr(L, name).restype = i
@@ -129,6 +130,20 @@ def gpt_attn_backward(h, x, W_attn, W_proj, dY, dx, dW_attn, db_attn, dW_proj, d
                                  _ptr(dW_attn), _ptr(db_attn), _ptr(dW_proj), _ptr(db_proj),
                                  B, T, _stream(stream))
     _check(rc, "gpt_attn_backward")
+
+
+NOALLOC_SCRATCH_BYTES = 80 << 20
+
+
+def gpt_attn_forward_noalloc(x, W_attn, b_attn, W_proj, b_proj, n_head, y, stream=None,
+                             B=None, T=None, C=None):
+    """x [B,T,C] -> y [B,T,C] (bf16 device tensors) without a handle and
+    without allocating: intermediates in the library's static scratch."""
+    if B is None or T is None or C is None:
+        B, T, C = int(x.shape[0]), int(x.shape[1]), int(x.shape[2])
+    rc = lib().gpt_attn_forward_noalloc(_ptr(x), B, T, C, n_head, _ptr(W_attn), _ptr(b_attn),
+                                        _ptr(W_proj), _ptr(b_proj), _ptr(y), _stream(stream))
+    _check(rc, "gpt_attn_forward_noalloc")
 
 
 def gpt_attn_set_dropout(h, p, seed):

@@ -45,7 +45,8 @@ extern "C" {
 enum gpt_attn_status {
   GPT_ATTN_OK = 0,
   GPT_ATTN_ERR_INVALID_ARG = 1, /* NULL pointer, non-positive size, bad dtype   */
-  GPT_ATTN_ERR_SHAPE = 2,       /* C % n_head != 0, n_head mismatch, B/T > max  */
+  GPT_ATTN_ERR_SHAPE = 2,       /* C % n_head != 0, n_head mismatch, B/T > max,
+                                   or above the allocation-free scratch        */
   GPT_ATTN_ERR_UNSUPPORTED = 3, /* head size other than 32 or 64                */
   GPT_ATTN_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned      */
   GPT_ATTN_ERR_OOM = 5,         /* workspace allocation failed                  */
@@ -155,6 +156,31 @@ int gpt_attn_destroy(gpt_attn_t h);
  * owns the events and must keep them alive while recording is on.
  * Errors: INVALID_ARG (NULL handle, or events non-NULL with n < 4). */
 int gpt_attn_set_stage_events(gpt_attn_t h, void *const *events, int n);
+
+/* Bytes of the static device scratch of gpt_attn_forward_noalloc. */
+#define GPT_ATTN_NOALLOC_SCRATCH_BYTES (80u << 20)
+
+/* Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Computes what gpt_attn_forward computes on a bf16 handle with
+ * dropout off and no state kept for a backward (the same kernels), without a
+ * handle and without any allocation: the intermediates (q, k, v, the merged
+ * heads, split-K partial sums of short sequences) live in a static device
+ * array of GPT_ATTN_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * every GPU it has run on until the process ends.  Element type bf16;
+ * tensors and their layouts as in gpt_attn_forward, on the current device;
+ * C = n_embd.  The array keeps the last call's contents; every call on one
+ * GPU uses the same array, so calls that overlap on one GPU (on different
+ * streams or from several host threads) race.  B = 0 or T = 0 is a no-op.
+ * Errors: INVALID_ARG (NULL tensor, negative or non-positive size),
+ * SHAPE (C % n_head != 0, or the intermediates -- 3*B*T*C and B*T*C bf16
+ * values, each rounded up to 256 bytes -- exceed
+ * GPT_ATTN_NOALLOC_SCRATCH_BYTES; the GPT-2 124M workload B = 12, T = 1024,
+ * C = 768 needs 75.5 MB), UNSUPPORTED (hs not in {32, 64}), ALIGN, HIP. */
+int gpt_attn_forward_noalloc(const void *x, int B, int T, int C, int n_head,
+                             const void *W_attn, const void *b_attn,
+                             const void *W_proj, const void *b_proj, void *y,
+                             void *stream);
 
 /* Static description of a status code (never NULL). */
 const char *gpt_attn_strerror(int code);
