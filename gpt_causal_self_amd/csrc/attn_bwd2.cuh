@@ -167,27 +167,24 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
   const int kv_end = min(T, (qt + 1) * 128);
   const int nkv = (kv_end + BKV - 1) / BKV;
 
-  // Loop-invariant per-lane source offsets within a tile; only a tile that
-  // crosses T checks rows (rows past T read a zero chunk).
-  int src_off[LPW];
+  // Loop-invariant per-lane byte offsets within a tile, loads through buffer
+  // resources over the (b, h) slabs of K and V: a tile at key j0 adds the
+  // wave-uniform j0 * HS * 2, and rows past T read zeros.
+  const __amdgpu_buffer_rsrc_t rk = slab_rsrc(Kh, (uint32_t)T * HS * 2);
+  const __amdgpu_buffer_rsrc_t rv = slab_rsrc(Vh, (uint32_t)T * HS * 2);
+  uint32_t src_off[LPW];
 #pragma unroll
   for (int q = 0; q < LPW; ++q) {
     const int row = (wid * LPW + q) * RPI + lane / CPR;
-    src_off[q] = row * HS + ((lane % CPR) ^ kv_swz<HS>(row)) * 8;
+    src_off[q] = (uint32_t)(row * HS + ((lane % CPR) ^ kv_swz<HS>(row)) * 8) * 2;
   }
   auto issue = [&](char* dst, int j0) {
-    const bf16_t* kt0 = Kh + (size_t)j0 * HS;
-    const bf16_t* vt0 = Vh + (size_t)j0 * HS;
-    const bool full = j0 + BKV <= T;
+    const uint32_t so = (uint32_t)j0 * HS * 2;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
-      const int row = (wid * LPW + q) * RPI + lane / CPR;
-      const bool ok = full || j0 + row < T;
-      const bf16_t* gk = ok ? kt0 + src_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
-      const bf16_t* gv = ok ? vt0 + src_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
       char* base = dst + (wid * LPW + q) * 1024;
-      __builtin_amdgcn_load_to_lds((void*)gk, GA_LDS(base), 16, 0, 0);
-      __builtin_amdgcn_load_to_lds((void*)gv, GA_LDS(base + TILE), 16, 0, 0);
+      buffer_to_lds16(rk, base, src_off[q], so);
+      buffer_to_lds16(rv, base + TILE, src_off[q], so);
     }
   };
   issue(smem, 0);
@@ -393,31 +390,29 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
   const float* Drow = Dpad + (size_t)bh * Tpad;
   const KeepBitsLayout kl(T);
 
-  // Loop-invariant per-lane (row, chunk) of each load; a query tile at i0
-  // adds i0 rows.  Only a tile that crosses T checks rows.
-  int q_off[LPW], o_off[LPW];
+  // Loop-invariant per-lane byte offsets of each load's (row, chunk), loads
+  // through buffer resources: Q's (b, h) slab, and dO's rows of (b, h) (row
+  // stride C, the head's HS columns; the resource ends after row T - 1's
+  // columns, so rows past T read zeros).  A query tile at i0 adds the
+  // wave-uniform offset of i0 rows.
+  const bf16_t* dOh = dOg + (size_t)b * T * C + h * HS;
+  const __amdgpu_buffer_rsrc_t rq = slab_rsrc(Qh, (uint32_t)T * HS * 2);
+  const __amdgpu_buffer_rsrc_t ro = slab_rsrc(dOh, ((uint32_t)(T - 1) * C + HS) * 2);
+  uint32_t q_off[LPW], o_off[LPW];
 #pragma unroll
   for (int q = 0; q < LPW; ++q) {
     const int row = (wid * LPW + q) * RPI + lane / CPR;
     const int c8 = ((lane % CPR) ^ kv_swz<HS>(row)) * 8;
-    q_off[q] = row * HS + c8;
-    o_off[q] = row * C + c8;
+    q_off[q] = (uint32_t)(row * HS + c8) * 2;
+    o_off[q] = (uint32_t)(row * C + c8) * 2;
   }
-  const bf16_t* dOh = dOg + (size_t)b * T * C + h * HS;
   auto issue = [&](char* dst, int i0) {
-    const bf16_t* qt0 = Qh + (size_t)i0 * HS;
-    const bf16_t* ot0 = dOh + (size_t)i0 * C;
-    const bool full = i0 + BQ <= T;
+    const uint32_t sq = (uint32_t)i0 * HS * 2, so = (uint32_t)i0 * C * 2;
 #pragma unroll
     for (int q = 0; q < LPW; ++q) {
-      const int inst = wid * LPW + q;
-      const int row = inst * RPI + lane / CPR;
-      const bool ok = full || i0 + row < T;
-      const bf16_t* gq = ok ? qt0 + q_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
-      const bf16_t* go = ok ? ot0 + o_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
-      char* base = dst + inst * 1024;
-      __builtin_amdgcn_load_to_lds((void*)gq, GA_LDS(base), 16, 0, 0);
-      __builtin_amdgcn_load_to_lds((void*)go, GA_LDS(base + TILE), 16, 0, 0);
+      char* base = dst + (wid * LPW + q) * 1024;
+      buffer_to_lds16(rq, base, q_off[q], sq);
+      buffer_to_lds16(ro, base + TILE, o_off[q], so);
     }
     // L and D of the 64 queries (rows padded to Tpad, so always in bounds):
     // lanes 0..15 of wave 0 fetch L, lanes 16..31 D, 16 bytes each

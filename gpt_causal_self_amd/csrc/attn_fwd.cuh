@@ -38,6 +38,38 @@ namespace gpt_attn {
 constexpr int kAttnBQ = 128;  // queries per block (bf16 kernel)
 constexpr int kAttnBK = 64;   // keys per tile
 
+// Reductions over the lane pairs (l, l ^ 32) of a wave with
+// v_permlane32_swap: the swap of a value with itself hands every lane both
+// x[l % 32] and x[l % 32 + 32], so the pair's max or sum needs no LDS
+// round trip (a __shfl_xor goes through ds_bpermute).  Both lanes of a pair
+// get the same value, formed in the same order.
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource of a bf16 slab of n_bytes bytes at p: raw (stride 0)
+// addressing, 32-bit data format; loads at byte offsets at or beyond
+// n_bytes return zeros, which is how a tile that crosses the sequence end
+// reads its missing rows.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* p, uint32_t n_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n_bytes,
+                                           0x00020000);
+}
+// 16 bytes per lane from the slab at voffset + soffset (bytes) straight into
+// LDS at lds (+ 16 * lane).
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds,
+                                                uint32_t voffset, uint32_t soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, soffset, 0, 0);
+}
+
 
 // ----------------------------------------------------- bf16, pipelined
 // Details of the bf16 kernel:
@@ -153,37 +185,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
   const int kv_end = min(T, (qt + 1) * kAttnBQ);
   const int nkv = (kv_end + BKV - 1) / BKV;
 
-  // Loads of the K and V tile starting at key j0 into the ring stage at dst.
-  // Per-lane source offsets within a tile are loop-invariant: lane -> (row,
-  // chunk) of load q; a tile at key j0 adds j0 * HS.  Only a tile that
-  // crosses T needs the row check (rows past T read a zero chunk).
-  int src_off[LPW];
+  // Loads of the K and V tile starting at key j0 into the ring stage at dst,
+  // through buffer resources over the (b, h) slabs of K and V: the per-lane
+  // byte offset within a tile is loop-invariant (lane -> (row, chunk) of
+  // load q), the tile's start j0 * HS * 2 is a wave-uniform offset, and
+  // rows past T lie beyond the slab and read zeros.
+  const __amdgpu_buffer_rsrc_t rk = slab_rsrc(Kh, (uint32_t)T * HS * 2);
+  const __amdgpu_buffer_rsrc_t rv = slab_rsrc(Vh, (uint32_t)T * HS * 2);
+  uint32_t src_off[LPW];
 #pragma unroll
   for (int q = 0; q < LPW; ++q) {
     const int row = (wid * LPW + q) * RPI + lane / CPR;
-    src_off[q] = row * HS + ((lane % CPR) ^ kv_swz<HS>(row)) * 8;
+    src_off[q] = (uint32_t)(row * HS + ((lane % CPR) ^ kv_swz<HS>(row)) * 8) * 2;
   }
   auto issue = [&](char* dst, int j0) {
-    const bf16_t* kt0 = Kh + (size_t)j0 * HS;
-    const bf16_t* vt0 = Vh + (size_t)j0 * HS;
-    if (j0 + BKV <= T) {
+    const uint32_t so = (uint32_t)j0 * HS * 2;
 #pragma unroll
-      for (int q = 0; q < LPW; ++q) {
-        char* base = dst + (wid * LPW + q) * 1024;
-        __builtin_amdgcn_load_to_lds((void*)(kt0 + src_off[q]), GA_LDS(base), 16, 0, 0);
-        __builtin_amdgcn_load_to_lds((void*)(vt0 + src_off[q]), GA_LDS(base + TILE), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < LPW; ++q) {
-        const int row = (wid * LPW + q) * RPI + lane / CPR;
-        const bool ok = j0 + row < T;
-        const bf16_t* gk = ok ? kt0 + src_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
-        const bf16_t* gv = ok ? vt0 + src_off[q] : reinterpret_cast<const bf16_t*>(&g_zero16);
-        char* base = dst + (wid * LPW + q) * 1024;
-        __builtin_amdgcn_load_to_lds((void*)gk, GA_LDS(base), 16, 0, 0);
-        __builtin_amdgcn_load_to_lds((void*)gv, GA_LDS(base + TILE), 16, 0, 0);
-      }
+    for (int q = 0; q < LPW; ++q) {
+      char* base = dst + (wid * LPW + q) * 1024;
+      buffer_to_lds16(rk, base, src_off[q], so);
+      buffer_to_lds16(rv, base + TILE, src_off[q], so);
     }
   };
 
@@ -249,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sc[kt][r]);
-    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    smax = pair_max32(smax);
     const float tmax = smax * scale_log2;
     // ---- lazy rescale (wave-uniform branch).  The reference is a whole
     // number (log2 units), so every weight is the true softmax weight times a
@@ -277,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
         sc[kt][r] = p;
         rs += p;
       }
-    rs += __shfl_xor(rs, 32);
+    rs = pair_sum32(rs);
     l += rs;
     if constexpr (DROP) {
       // keys j0 + kt*32 + 8g + 4hi + e (e = 0..3) of query myq: one Philox
