@@ -198,50 +198,46 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
     constexpr bool MASK = decltype(mask_tag)::value;
     if (jn >= 0) issue(wr, jn);
     const lds_char* lbase = (const lds_char*)rd;
-    floatx16 sc[2], dp[2];
+    // one 32-key half at a time: its scores, softmax gradient and dQ product
+    // (half the score registers live, for three waves per SIMD)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      floatx16 sc, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        sc[kt][r] = 0.f;
-        dp[kt][r] = 0.f;
+        sc[r] = 0.f;
+        dp[r] = 0.f;
       }
 #pragma unroll
       for (int kk = 0; kk < HS / 16; ++kk) {
         const bf16x8 kf = *(lds_b128*)(lbase + koff[kk] + kt * 32 * RB);
         const bf16x8 vf = *(lds_b128*)(lbase + TILE + koff[kk] + kt * 32 * RB);
-        sc[kt] = mfma32(kf, qf[kk], sc[kt]);
-        dp[kt] = mfma32(vf, gf[kk], dp[kt]);
+        sc = mfma32(kf, qf[kk], sc);
+        dp = mfma32(vf, gf[kk], dp);
       }
-    }
-    // lane = query myq; register r of kt <-> key j0 + kt*32 + 8(r/4) + 4hi + r%4
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      // lane = query myq; register r <-> key j0 + kt*32 + 8(r/4) + 4hi + r%4
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sc[kt][r], scale_log2, -L2));
-          float dpv = dp[kt][r];
+          const float p = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, -L2));
+          float dpv = dp[r];
           if constexpr (DROP) dpv *= ((kw >> (16 * kt + r)) & 1u) ? drop.scale : 0.f;
           float ds = p * (dpv - Dq);
           if constexpr (MASK) {
             const int key = j0 + kt * 32 + 8 * g + 4 * hi + e;
             if (key > myq) ds = 0.f;
           }
-          dp[kt][r] = ds;
+          dp[r] = ds;
         }
       }
-    }
-    // dQ^T += K^T dS^T; K^T by transposing reads in the key order of dS
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      // dQ^T += K^T dS^T; K^T by transposing reads in the key order of dS
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         bf16x8 sf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sf[e] = (__bf16)dp[kt][8 * u + e];
+        for (int e = 0; e < 8; ++e) sf[e] = (__bf16)dp[8 * u + e];
         const int kb = kt * 32 + 16 * u;
 #pragma unroll
         for (int dt = 0; dt < HS / 32; ++dt) {
@@ -256,6 +252,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq2_bf16_kernel(
           dq[dt] = mfma32(__builtin_bit_cast(bf16x8, kv), sf, dq[dt]);
         }
       }
+    }
   };
 
   // keep bits: the word of tile it + 1 is loaded during tile it (before its

@@ -50,7 +50,8 @@ def _ln_gpu(x, w, b):
 
 @pytest.mark.parametrize("M,C,bias,offset", [
     (300, 256, True, 0.0), (12288, 768, True, 0.0), (37, 1600, False, 0.0), (5, 8, True, 0.0),
-    (9, 8192, True, 0.0), (64, 768, True, 40.0)])
+    (9, 8192, True, 0.0), (64, 768, True, 40.0), (13, 512, True, 0.0), (301, 768, False, 0.0),
+    (7, 1024, True, 0.0)])
 def test_layernorm(M, C, bias, offset):
     from gpt_causal_self_amd.inputs import to_dtype
     rng = np.random.default_rng(M + C)
