@@ -433,9 +433,13 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
   typedef float f4v __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) const f4v lds_f4;
 
-  auto tile = [&](auto mask_tag, const char* __restrict__ rd, char* __restrict__ wr, int in,
-                  int i0) {
+  // MASK: the tile reaches the keys' diagonal; RAGGED: it may hold queries
+  // at or past T (rows whose Q and dO read zeros, and whose L and D pad
+  // entries are never written), which are zeroed explicitly
+  auto tile = [&](auto mask_tag, auto ragged_tag, const char* __restrict__ rd,
+                  char* __restrict__ wr, int in, int i0) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool RAGGED = decltype(ragged_tag)::value;
     if (in >= 0) issue(wr, in);
     const lds_char* lbase = (const lds_char*)rd;
     floatx16 s[2], dp[2];
@@ -482,7 +486,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
             s[qh][r] = p;
             dp[qh][r] = p * (dpv - Ds[e]);
           }
-          const bool dead = q >= T || (MASK && mykey > q);
+          const bool dead = (RAGGED && q >= T) || (MASK && mykey > q);
           if (dead) {
             s[qh][r] = 0.f;
             dp[qh][r] = 0.f;
@@ -535,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
     const int in = it + 1 < nqt ? i0 + BQ : -1;
     char* wr = smem + ((it + 1) & 1) * STAGE;
     if (i0 + BQ - 1 >= kw0)
-      tile(std::integral_constant<bool, true>{}, smem + (it & 1) * STAGE, wr, in, i0);
+      tile(std::true_type{}, std::true_type{}, smem + (it & 1) * STAGE, wr, in, i0);
     else if (in >= 0)
       issue(wr, in);
   }
@@ -544,8 +548,12 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
     bar_nofence();
     const int i0 = kb0 + it * BQ;
     const int in = it + 1 < nqt ? i0 + BQ : -1;
-    tile(std::integral_constant<bool, false>{}, smem + (it & 1) * STAGE,
-         smem + ((it + 1) & 1) * STAGE, in, i0);
+    char* rd = smem + (it & 1) * STAGE;
+    char* wr = smem + ((it + 1) & 1) * STAGE;
+    if (i0 + BQ <= T)
+      tile(std::false_type{}, std::false_type{}, rd, wr, in, i0);
+    else
+      tile(std::false_type{}, std::true_type{}, rd, wr, in, i0);
   }
 
   if (mykey < T) {
