@@ -550,10 +550,15 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv2_bf16_kernel(
     const int in = it + 1 < nqt ? i0 + BQ : -1;
     char* rd = smem + (it & 1) * STAGE;
     char* wr = smem + ((it + 1) & 1) * STAGE;
-    if (i0 + BQ <= T)
-      tile(std::false_type{}, std::false_type{}, rd, wr, in, i0);
-    else
-      tile(std::false_type{}, std::true_type{}, rd, wr, in, i0);
+    // (with dropout the kernel keeps one body: a second copy of the loop
+    // body pushes it past the register file)
+    if constexpr (!DROP) {
+      if (i0 + BQ <= T) {
+        tile(std::false_type{}, std::false_type{}, rd, wr, in, i0);
+        continue;
+      }
+    }
+    tile(std::false_type{}, std::true_type{}, rd, wr, in, i0);
   }
 
   if (mykey < T) {
