@@ -415,8 +415,12 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
                          sd, cpart, bcs, N3, (bf16_t*)db_attn);
     }
     Epi2RowMajor e_dx{(bf16_t*)dx, C, nullptr};
-    launch_gemm2<GA_DGRAD_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3, e_dx,
-                                            st);
+    if (use_gemm3(M, C))
+      launch_gemm3<GA_DGRAD3_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3,
+                                               e_dx, st);
+    else
+      launch_gemm2<GA_DGRAD_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3,
+                                              e_dx, st);
     (void)hipEventRecord(h->ev_join, sd);
     (void)hipStreamWaitEvent(st, h->ev_join, 0);
   } else {

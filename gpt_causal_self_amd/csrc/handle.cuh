@@ -21,6 +21,16 @@
 #ifndef GA_DGRAD_TILE
 #define GA_DGRAD_TILE 192, 256, 2, 64, 2, 4
 #endif
+// Projections onto C columns with C a multiple of 384 and at least 128 such
+// tiles: the GEMM whose loader and MFMA waves sit on separate SIMDs
+// (gemm3.cuh), 96 x 384 tiles (BM, BN, stages, BK, wave grid of six):
+// the forward c_proj (K = C) and the dx product of the backward (K = 3C).
+#ifndef GA_PROJ3_TILE
+#define GA_PROJ3_TILE 96, 384, 4, 32, 1, 6
+#endif
+#ifndef GA_DGRAD3_TILE
+#define GA_DGRAD3_TILE 96, 384, 2, 64, 1, 6
+#endif
 #ifndef GA_ATTN_STAGES
 #define GA_ATTN_STAGES 2
 #endif

@@ -2,10 +2,13 @@
 // gpt_attn_forward and the Pre-LN block entry point.
 #pragma once
 
+#include <type_traits>
+
 #include <algorithm>
 
 #include "attn_fwd.cuh"
 #include "gemm2.cuh"
+#include "gemm3.cuh"
 #include "skinny.cuh"
 #include "handle.cuh"
 
@@ -181,6 +184,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void skinny_epi_kernel(const bf16_t
   }
 }
 
+// Whether a projection onto N columns over M rows takes gemm3's 96 x 384
+// tiles: N a multiple of 384 (no partly empty column tile) and at least 128
+// tiles (enough blocks without a split of K).
+inline bool use_gemm3(int M, int N) {
+  return N % 384 == 0 && (long)((M + 95) / 96) * (N / 384) >= 128;
+}
+
 // The projection GEMM, split along K when it has fewer than 128 output
 // tiles: up to 8 slices (each at least 2 k-tiles), as many as give about
 // 256 blocks and fit the partial buffer.
@@ -192,6 +202,12 @@ inline void launch_proj(const gpt_attn_handle* h, const bf16_t* A, int lda, cons
     if (M <= GA_SKINNY_MAX_M && N % kDecCols == 0 && K % 8 == 0 && ldb == N) {
       hipLaunchKernelGGL(skinny_epi_kernel<Epi>, dim3(N / kDecCols, (M + 15) / 16),
                          dim3(64 * kDecWaves), skinny_lds_bytes(), st, A, lda, M, K, Bm, N, epi);
+      return;
+    }
+  }
+  if constexpr (std::is_same<Epi, Epi2RowMajor>::value && A_KC && !B_KC) {
+    if (use_gemm3(M, N)) {
+      launch_gemm3<GA_PROJ3_TILE, true, false>(A, lda, Bm, ldb, M, N, K, epi, st);
       return;
     }
   }

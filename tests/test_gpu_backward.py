@@ -86,6 +86,14 @@ def test_backward_training_step_workload_full():
               f"normwise vs exact {rel:.2e}", flush=True)
 
 
+def test_backward_ragged_rows_wide_projection():
+    """B*T = 6600 rows at C = 768: the dx product runs on 96 x 384 tiles
+    (138 of them, the last row tile 72 rows deep), every gradient against the
+    fp64 oracle."""
+    inp = make_inputs(6, 1100, 768, 12, dtype="bf16", seed=66, with_dY=True)
+    check_grads(inp)
+
+
 def test_backward_deterministic():
     inp = make_inputs(2, 200, 768, 12, dtype="bf16", seed=31, with_dY=True)
     a = gpu_train_step(inp)

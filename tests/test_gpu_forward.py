@@ -60,6 +60,15 @@ def test_workload_gpt2_shapes_full(index):
     _check(workload_inputs(index))
 
 
+def test_ragged_rows_wide_projection():
+    """B*T = 7000 rows at C = 768: c_proj runs on 96 x 384 tiles (146 of them,
+    the last row tile 88 rows deep); the first sequence and the last two
+    (which hold the ragged tile) against the oracle, stages included."""
+    inp = make_inputs(7, 1000, 768, 12, dtype="bf16", seed=70)
+    _check(inp, batches=(0, 1))
+    _check(inp, batches=(5, 7))
+
+
 @pytest.mark.parametrize("T", WORKLOADS[4].ragged_T)
 def test_workload_gpt2_xl_ragged(T):
     """Every sequence of each prefix length, stages included."""
