@@ -2,7 +2,8 @@
 // different SIMDs.
 //
 // C[m][n] = sum_k A(m,k) B(k,n), fp32 accumulation, handed to a staged
-// epilogue (bias, activation, rounding, 16-byte runs of a row; gemm2.cuh).
+// epilogue (bias, activation, rounding, 16-byte runs of a row; or, for
+// epilogues that read memory per run, acc + bias in fp32; gemm2.cuh).
 // Operand layouts and LDS swizzles as in gemm2.cuh.
 //
 // Why.  On gfx950 a global load (direct-to-LDS or into registers) issued by a
@@ -130,6 +131,38 @@ __device__ __forceinline__ bf16x8 g3_frag(const char* lds, int rb, int kk, int l
   }
 }
 
+// fp32-staged epilogue block (epilogues that read memory per run, e.g. a
+// residual): the LDS block cf [32][BN + 4] holds acc + bias of tile rows
+// 32 i .. 32 i + 31; all eight waves hand its 8-column runs to store8f, with
+// the epilogue's Extra8 of all their runs loaded before the first store (a
+// load after a store waits for it: they may alias).
+template <int BN, class Epi>
+__device__ __forceinline__ void g3_store_f32_block(const float* cf, const Epi& epi, int i, int m0,
+                                                   int n0, int M, int N, int tid) {
+  constexpr int SPF = BN + 4;
+  constexpr int kRuns = 32 * BN / 8;
+  constexpr int kPass = (kRuns + 64 * kG3Waves - 1) / (64 * kG3Waves);
+  typename Epi::Extra8 ex[kPass];
+#pragma unroll
+  for (int p = 0; p < kPass; ++p) {
+    const int c = tid + p * 64 * kG3Waves;
+    const int m = m0 + i * 32 + c / (BN / 8), n = n0 + (c % (BN / 8)) * 8;
+    ex[p] = epi.extra8(m, n, c < kRuns && m < M && n < N);
+  }
+#pragma unroll
+  for (int p = 0; p < kPass; ++p) {
+    const int c = tid + p * 64 * kG3Waves;
+    const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+    const int m = m0 + i * 32 + rl, n = n0 + cl;
+    if (c < kRuns && m < M && n < N) {
+      const float4 a = *reinterpret_cast<const float4*>(cf + rl * SPF + cl);
+      const float4 b = *reinterpret_cast<const float4*>(cf + rl * SPF + cl + 4);
+      const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      epi.store8f(m, n, v, ex[p]);
+    }
+  }
+}
+
 template <int BM, int BN, int BK, int NSTAGE, bool A_KC, bool B_KC, int WGM, int WGN, class Epi>
 __global__ __launch_bounds__(64 * kG3Waves) void gemm3_kernel(const bf16_t* __restrict__ A,
                                                               int lda,
@@ -137,8 +170,9 @@ __global__ __launch_bounds__(64 * kG3Waves) void gemm3_kernel(const bf16_t* __re
                                                               int ldb, int M, int N, int K,
                                                               Epi epi) {
   static_assert(WGM * WGN == kG3Waves - kG3Loaders, "six MFMA waves");
-  static_assert(Staged<Epi>::value && !StagedF32<Epi>::value && !Store8All<Epi>::value,
-                "bf16 staged epilogues only");
+  static_assert(Staged<Epi>::value && !Store8All<Epi>::value, "staged epilogues");
+  constexpr bool kF32 = StagedF32<Epi>::value;
+  static_assert(!kF32 || WGM == 1, "fp32 staging goes by 32-row blocks of a one-row wave grid");
   static_assert(BK == 64 || BK == 32, "BK");
   static_assert(B_KC || (BN / 8) % 2 == 0, "row-contiguous tile");
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -149,7 +183,9 @@ __global__ __launch_bounds__(64 * kG3Waves) void gemm3_kernel(const bf16_t* __re
   constexpr int kRing = NSTAGE * kStage;
   constexpr int SP = BN + 8;  // staged epilogue pitch (elements)
   constexpr int kEpiBytes = BM * SP * 2;
-  static_assert(kEpiBytes <= kRing, "the staged tile reuses the ring");
+  constexpr int SPF = BN + 4;  // fp32 staging pitch (floats), 32 rows at a time
+  static_assert(kF32 ? 32 * SPF * 4 <= kRing : kEpiBytes <= kRing,
+                "the staged tile reuses the ring");
   constexpr int kBiasOff = (kRing + 15) / 16 * 16;
   static_assert(kBiasOff + BN * 2 <= 160 * 1024, "LDS");
   constexpr int kLoadsA = G3Off<BM, BK, A_KC>::kPerWave, kLoadsB = G3Off<BN, BK, B_KC>::kPerWave;
@@ -175,6 +211,7 @@ __global__ __launch_bounds__(64 * kG3Waves) void gemm3_kernel(const bf16_t* __re
   const int nk = (K + BK - 1) / BK;
 
   bf16_t* ct = reinterpret_cast<bf16_t*>(smem);
+  float* cf = reinterpret_cast<float*>(smem);
   // The two roles run separate loops with the same barriers, so that the
   // loaders' offsets and the accumulators are never live together.
   if (loader) {
@@ -213,6 +250,15 @@ __global__ __launch_bounds__(64 * kG3Waves) void gemm3_kernel(const bf16_t* __re
         g3_issue<BN, BK, B_KC>(Bm, ldb, n0, N, kn * BK, K, sw + kA, li, lane, pb);
       }
     }
+    if constexpr (kF32) {
+#pragma unroll 1
+      for (int i = 0; i < MT; ++i) {
+        bar_nofence();  // the ring / the previous block's runs are free
+        bar_after_lds_writes();
+        g3_store_f32_block<BN>(cf, epi, i, m0, n0, M, N, tid);
+      }
+      return;
+    }
     bar_nofence();  // the ring is free for the staged tile
   } else {
     floatx16 acc[MT][NT];
@@ -239,6 +285,27 @@ __global__ __launch_bounds__(64 * kG3Waves) void gemm3_kernel(const bf16_t* __re
           for (int j = 0; j < NT; ++j) acc[i][j] = mfma32(bfr[j], af[i], acc[i][j]);
       }
     }
+    if constexpr (kF32) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        bar_nofence();  // the ring / the previous block's runs are free
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int cl = wn * WTN + j * 32 + 8 * g + 4 * (lane >> 5);
+            const uint2 bu = *reinterpret_cast<const uint2*>(smem + kBiasOff + cl * 2);
+            const float b[4] = {bf2f(bu.x & 0xffff), bf2f(bu.x >> 16), bf2f(bu.y & 0xffff),
+                                bf2f(bu.y >> 16)};
+            *reinterpret_cast<float4*>(cf + (lane & 31) * SPF + cl) =
+                make_float4(acc[i][j][4 * g] + b[0], acc[i][j][4 * g + 1] + b[1],
+                            acc[i][j][4 * g + 2] + b[2], acc[i][j][4 * g + 3] + b[3]);
+          }
+        bar_after_lds_writes();
+        g3_store_f32_block<BN>(cf, epi, i, m0, n0, M, N, tid);
+      }
+      return;
+    }
     bar_nofence();  // every wave is done with the ring
     // staged epilogue: bias + acc (rounded, with the epilogue's activation)
     // into an LDS tile [BM][BN + 8] over the ring
@@ -264,12 +331,14 @@ __global__ __launch_bounds__(64 * kG3Waves) void gemm3_kernel(const bf16_t* __re
       }
   }
   // all eight waves store 16-byte runs of the staged rows
-  bar_after_lds_writes();
-  constexpr int kChunks = BM * BN / 8;
-  for (int c = tid; c < kChunks; c += 64 * kG3Waves) {
-    const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
-    const int m = m0 + rl, n = n0 + cl;
-    if (m < M && n < N) epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
+  if constexpr (!kF32) {
+    bar_after_lds_writes();
+    constexpr int kChunks = BM * BN / 8;
+    for (int c = tid; c < kChunks; c += 64 * kG3Waves) {
+      const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+      const int m = m0 + rl, n = n0 + cl;
+      if (m < M && n < N) epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
+    }
   }
 }
 

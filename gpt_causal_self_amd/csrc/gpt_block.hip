@@ -81,14 +81,25 @@ int gpt_mlp_forward(const void* x, int M, int C, int F, const void* W_fc, const 
   const hipStream_t st = as_stream(stream);
   Epi2Gelu e1{(bf16_t*)hbuf, F, (const bf16_t*)b_fc};
   launch_gemm2<GA_FC_TILE>((const bf16_t*)x, C, (const bf16_t*)W_fc, F, M, F, C, e1, st);
+  // c_proj [4C -> C]: the split-role GEMM on 96 x 384 tiles where C allows
+  // (csrc/gemm3.cuh), else gemm2
+  const bool g3 = use_gemm3(M, C);
   if (residual) {
     Epi2RowMajorRes e2{(bf16_t*)y, C, (const bf16_t*)b_proj, (const bf16_t*)residual};
-    launch_gemm2<GA_FCPROJ_TILE>((const bf16_t*)hbuf, F, (const bf16_t*)W_proj, C, M, C, F, e2,
-                                 st);
+    if (g3)
+      launch_gemm3<GA_PROJ3_TILE, true, false>((const bf16_t*)hbuf, F, (const bf16_t*)W_proj, C,
+                                               M, C, F, e2, st);
+    else
+      launch_gemm2<GA_FCPROJ_TILE>((const bf16_t*)hbuf, F, (const bf16_t*)W_proj, C, M, C, F,
+                                   e2, st);
   } else {
     Epi2RowMajor e2{(bf16_t*)y, C, (const bf16_t*)b_proj};
-    launch_gemm2<GA_FCPROJ_TILE>((const bf16_t*)hbuf, F, (const bf16_t*)W_proj, C, M, C, F, e2,
-                                 st);
+    if (g3)
+      launch_gemm3<GA_PROJ3_TILE, true, false>((const bf16_t*)hbuf, F, (const bf16_t*)W_proj, C,
+                                               M, C, F, e2, st);
+    else
+      launch_gemm2<GA_FCPROJ_TILE>((const bf16_t*)hbuf, F, (const bf16_t*)W_proj, C, M, C, F,
+                                   e2, st);
   }
   return launch_status();
 }

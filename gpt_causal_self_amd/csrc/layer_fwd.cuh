@@ -205,7 +205,10 @@ inline void launch_proj(const gpt_attn_handle* h, const bf16_t* A, int lda, cons
       return;
     }
   }
-  if constexpr (std::is_same<Epi, Epi2RowMajor>::value && A_KC && !B_KC) {
+  if constexpr ((std::is_same<Epi, Epi2RowMajor>::value ||
+                 std::is_same<Epi, Epi2RowMajorRes>::value ||
+                 std::is_same<Epi, Epi2RowMajorDrop>::value) &&
+                A_KC && !B_KC) {
     if (use_gemm3(M, N)) {
       launch_gemm3<GA_PROJ3_TILE, true, false>(A, lda, Bm, ldb, M, N, K, epi, st);
       return;

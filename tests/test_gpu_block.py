@@ -122,6 +122,13 @@ def test_block_small(B, T, C, H, bias):
     _block_check(inp, ln_w, ln_b, _block_gpu(inp, ln_w, ln_b))
 
 
+def test_block_ragged_rows_wide_projection():
+    """7000 rows at C = 768: the residual c_proj on 96 x 384 tiles, the last
+    row tile 88 rows deep."""
+    inp, ln_w, ln_b = _block_inputs(7, 1000, 768, 12, seed=17)
+    _block_check(inp, ln_w, ln_b, _block_gpu(inp, ln_w, ln_b))
+
+
 def test_block_gpt2_124m_full():
     """GPT-2 124M shape (B=12, T=1024, C=768, 12 heads), every sequence."""
     inp, ln_w, ln_b = _block_inputs(12, 1024, 768, 12, seed=7)
@@ -210,7 +217,10 @@ def _mlp_check(m):
 @pytest.mark.parametrize("M,C,F,bias,res", [(300, 256, 1024, True, False),
                                              (257, 128, 512, False, True),
                                              (1, 64, 256, True, True),
-                                             (1000, 768, 3072, True, True)])
+                                             (1000, 768, 3072, True, True),
+                                             # 96 x 384 c_proj tiles, ragged last row tile
+                                             (7000, 768, 3072, True, True),
+                                             (6600, 768, 3072, False, False)])
 def test_mlp_small(M, C, F, bias, res):
     m = make_mlp_inputs(M, C, F, seed=M + F, bias=bias, with_residual=res,
                         proj_std=0.05)

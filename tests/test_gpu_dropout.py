@@ -57,7 +57,10 @@ def _check(g, r, what):
 
 
 @pytest.mark.parametrize("B,T,C,H,p,seed", [(2, 70, 256, 4, 0.1, 1), (3, 129, 128, 4, 0.5, 2),
-                                            (1, 64, 256, 8, 0.9, 3)])
+                                            (1, 64, 256, 8, 0.9, 3),
+                                            # 7000 rows at C = 768: the c_proj of 96 x 384
+                                            # tiles with a ragged last row tile
+                                            (7, 1000, 768, 12, 0.1, 4)])
 def test_dropout_forward_small(B, T, C, H, p, seed):
     inp = _inputs(B, T, C, H, seed=T + C)
     g = _fwd(inp, p, seed)
