@@ -48,7 +48,7 @@ N_SETS = 8
 COPY_BYTES = 1 << 30          # calibration copy: 1 GiB read + 1 GiB written
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_kernels_gpt2_124m_B12_T1024.md")
 KERNEL_KEYS = {"c_attn": ("gemm2_kernel", "Epi2QKV"), "attention": ("attn_fwd2_bf16_kernel",),
-               "c_proj": ("gemm2_kernel", "Epi2RowMajor")}
+               "c_proj": ("gemm3_kernel", "gpt_attn::Epi2RowMajor>")}
 
 
 def layer_flops(B, T, C):
@@ -346,8 +346,8 @@ def write_kernel_stats(stats_dir, out_md):
         M = B * T
         want = {"c_attn": ("Epi2QKV", (M // 256) * (3 * C // 256) * 512, 1),
                 "attention": ("attn_fwd2_bf16_kernel<64, 2, false>", B * H * 256, T // 128),
-                "c_proj": ("gemm2_kernel<192, 256, 64, 2, true, false, 2, 4, "
-                           "gpt_attn::Epi2RowMajor, 1>", (M // 192) * (C // 256) * 512, 1)}
+                "c_proj": ("gemm3_kernel<96, 384, 32, 4, true, false, 1, 6, "
+                           "gpt_attn::Epi2RowMajor>", ((M + 95) // 96) * (C // 384) * 512, 1)}
         durs = {k: [] for k in want}
         for r in csv.DictReader(open(traces[0])):
             for k, (name, gx, gy) in want.items():
