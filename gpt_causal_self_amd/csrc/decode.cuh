@@ -16,7 +16,7 @@
 //                        either scatters q / k / v (q to a buffer, k and v
 //                        into the caches at `pos`) or writes a row-major
 //                        output.
-//   decode_attn_kernel   per (b, h) and chunk of 128 cached keys per wave:
+//   decode_attn_kernel   per (b, h) and chunk of KPW cached keys per wave:
 //                        scores, max, exp2 weights, sum and the weighted
 //                        value sum; HBM-bound on the cache.  With one chunk
 //                        (pos + 1 <= chunk) the block writes the head; with
@@ -121,25 +121,28 @@ __global__ __launch_bounds__(64 * kDecWaves) void skinny_gemm_kernel(
 }
 
 // Attention of one query per (b, h) over cached keys [chunk * CHUNK,
-// min(pos + 1, (chunk + 1) * CHUNK)), CHUNK = 128 keys per wave of the NT
-// threads.  Each wave takes 128
-// consecutive keys and runs on its own as its loads arrive: lane l scores
-// keys l and l + 64, the wave takes its max, exp2 weights and sum, passes
-// the weights through its own LDS slice, and for the weighted value sum lane
-// l takes 8 value columns (dg) of a group of consecutive keys (kg); the
-// groups are summed with lane shuffles.  The 8 waves' (m, l, o) then merge
-// after the block's one barrier, each rescaled to the common maximum.  One
+// min(pos + 1, (chunk + 1) * CHUNK)), CHUNK = KPW keys per wave of the NT
+// threads.  Each wave takes KPW consecutive keys and runs on its own as its
+// loads arrive: lane l scores keys l, l + 64, ..., the wave takes its max,
+// exp2 weights and sum, passes the weights through its own LDS slice, and
+// for the weighted value sum lane l takes 8 value columns (dg) of a group of
+// consecutive keys (kg); the groups are summed with lane shuffles.  The
+// waves' (m, l, o) then merge after the block's one barrier, each rescaled
+// to the common maximum.  More, shorter waves per block keep more of the
+// cache's loads in flight on the block's CU (16 waves of 64 keys: a 1024-key
+// cache in one block).  One
 // chunk: the block writes y_m[b][h*HS + d] = bf16(o / l).  Several: it writes
 // (m, l, o[0..HS)) in fp32 (m the chunk's max of the log2-scaled scores,
 // l = sum 2^(s - m), o = sum 2^(s - m) v), and the last chunk block of the
 // (b, h) to finish merges the chunks the same way.
-template <int HS, int NT>
+template <int HS, int NT, int KPW>
 __global__ __launch_bounds__(NT) void decode_attn_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, float* __restrict__ part, bf16_t* __restrict__ ym, int H,
     int cache_T, int pos, int nchunk, float scale_log2, unsigned* __restrict__ counters) {
+  static_assert(KPW % 64 == 0, "a lane per key, KPW / 64 keys each");
   constexpr int NW = NT / 64;
-  constexpr int KPW = 128;                  // keys per wave
+  constexpr int KT = KPW / 64;              // keys per lane for the scores
   constexpr int CHUNK = NW * KPW;           // keys per block
   constexpr int DG = HS / 8, KG = 64 / DG;  // value columns / key groups per wave
   constexpr int KPG = KPW / KG;             // keys per group
@@ -160,9 +163,9 @@ __global__ __launch_bounds__(NT) void decode_attn_kernel(
     vr[u] = jb + u <= pos
                 ? *reinterpret_cast<const uint4*>(v_cache + head + (size_t)(jb + u) * HS + 8 * dg)
                 : make_uint4(0u, 0u, 0u, 0u);
-  uint4 kr[2][HS / 8];
+  uint4 kr[KT][HS / 8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < KT; ++t) {
     const int j = kw0 + lane + 64 * t;
 #pragma unroll
     for (int d8 = 0; d8 < HS / 8; ++d8)
@@ -170,10 +173,10 @@ __global__ __launch_bounds__(NT) void decode_attn_kernel(
                       ? *reinterpret_cast<const uint4*>(k_cache + head + (size_t)j * HS + 8 * d8)
                       : make_uint4(0u, 0u, 0u, 0u);
   }
-  float s[2];
+  float s[KT];
   float m = -INFINITY;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < KT; ++t) {
     const int j = kw0 + lane + 64 * t;
     float acc = 0.f;
 #pragma unroll
@@ -195,7 +198,7 @@ __global__ __launch_bounds__(NT) void decode_attn_kernel(
   // weights of keys past pos are 0 (also when the whole wave is past pos)
   float l = 0.f;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < KT; ++t) {
     const float p = kw0 + lane + 64 * t <= pos ? __builtin_amdgcn_exp2f(s[t] - m) : 0.f;
     ps[w][lane + 64 * t] = p;
     l += p;

@@ -9,10 +9,14 @@ using namespace gpt_attn;
 namespace {
 
 #ifndef GA_DEC_ATTN_THREADS
-#define GA_DEC_ATTN_THREADS 512
+#define GA_DEC_ATTN_THREADS 1024
 #endif
-constexpr int kDecAttnThreads = GA_DEC_ATTN_THREADS;  // 128 cached keys per wave
-constexpr int kDecChunk = kDecAttnThreads / 64 * 128;
+#ifndef GA_DEC_ATTN_KPW
+#define GA_DEC_ATTN_KPW 64
+#endif
+constexpr int kDecAttnThreads = GA_DEC_ATTN_THREADS;
+constexpr int kDecAttnKpw = GA_DEC_ATTN_KPW;  // cached keys per wave
+constexpr int kDecChunk = kDecAttnThreads / 64 * kDecAttnKpw;
 inline int nchunks(int n) { return (n + kDecChunk - 1) / kDecChunk; }
 
 }  // namespace
@@ -52,11 +56,11 @@ int gpt_attn_decode(gpt_attn_t h, const void* x_new, int B, int pos, const void*
                      dim3(64 * kDecWaves), skinny_lds_bytes(), st, (const bf16_t*)x_new, B,
                      C, (const bf16_t*)W_attn, 3 * C, (const bf16_t*)b_attn, o1);
   if (hs == 64)
-    hipLaunchKernelGGL((decode_attn_kernel<64, kDecAttnThreads>), dim3(B * H, nc), dim3(kDecAttnThreads), 0, st, q,
+    hipLaunchKernelGGL((decode_attn_kernel<64, kDecAttnThreads, kDecAttnKpw>), dim3(B * H, nc), dim3(kDecAttnThreads), 0, st, q,
                        (const bf16_t*)k_cache, (const bf16_t*)v_cache, part, ym, H, cache_T, pos,
                        nc, scale_log2, cnt_attn);
   else
-    hipLaunchKernelGGL((decode_attn_kernel<32, kDecAttnThreads>), dim3(B * H, nc), dim3(kDecAttnThreads), 0, st, q,
+    hipLaunchKernelGGL((decode_attn_kernel<32, kDecAttnThreads, kDecAttnKpw>), dim3(B * H, nc), dim3(kDecAttnThreads), 0, st, q,
                        (const bf16_t*)k_cache, (const bf16_t*)v_cache, part, ym, H, cache_T, pos,
                        nc, scale_log2, cnt_attn);
   DecRowOut o2{(bf16_t*)y, C};
