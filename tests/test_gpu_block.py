@@ -220,7 +220,9 @@ def _mlp_check(m):
                                              (1000, 768, 3072, True, True),
                                              # 96 x 384 c_proj tiles, ragged last row tile
                                              (7000, 768, 3072, True, True),
-                                             (6600, 768, 3072, False, False)])
+                                             (6600, 768, 3072, False, False),
+                                             # K = F = 3000: a partial last k-tile
+                                             (6600, 768, 3000, True, True)])
 def test_mlp_small(M, C, F, bias, res):
     m = make_mlp_inputs(M, C, F, seed=M + F, bias=bias, with_residual=res,
                         proj_std=0.05)
