@@ -37,9 +37,11 @@
 #ifndef GA_WGRAD_TILE
 #define GA_WGRAD_TILE 128, 128, 2, 64, 2, 2
 #endif
-// weight gradient of c_attn (C x 3C over all B*T rows): large tiles, one per CU
+// weight gradient of c_attn (C x 3C over all B*T rows): 256 x 128 tiles split
+// along the rows to about one block per CU (4 slices at C = 768: half the
+// fp32 partials that 256 x 256 tiles in 8 slices leave for the reduction)
 #ifndef GA_WGRAD_ATTN_TILE
-#define GA_WGRAD_ATTN_TILE 256, 256, 2, 64, 2, 4
+#define GA_WGRAD_ATTN_TILE 256, 128, 2, 64, 4, 2
 #endif
 #ifndef GA_WGRAD_ATTN_PER_CU
 #define GA_WGRAD_ATTN_PER_CU 1
