@@ -66,46 +66,6 @@ __device__ __forceinline__ float lane_group_sum(float v) {
   return v;
 }
 
-// Column sums of a bf16 matrix: block (x, y) sums columns [64x, 64x + 64)
-// over rows [y * rows_per, (y + 1) * rows_per); 256 threads = 8 column groups
-// (16-byte loads of 8 columns) x 32 row slots, the slot sums meet in LDS in a
-// fixed order; part[y][n] receives the block's sums.  N % 8 == 0.
-__global__ __launch_bounds__(256) void colsum_bf16_kernel(const bf16_t* __restrict__ X, int M,
-                                                          int N, int ld, int rows_per,
-                                                          float* __restrict__ part) {
-  __shared__ float red[32][64];
-  const int tid = threadIdx.x, cg = tid & 7, slot = tid >> 3;
-  const int n = blockIdx.x * 64 + 8 * cg;
-  const int r0 = blockIdx.y * rows_per, r1 = min(M, r0 + rows_per);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (n < N) {
-    for (int r = r0 + slot; r < r1; r += 32 * 4) {
-      uint4 u[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        u[q] = r + 32 * q < r1 ? *reinterpret_cast<const uint4*>(X + (size_t)(r + 32 * q) * ld + n)
-                               : make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const unsigned w[4] = {u[q].x, u[q].y, u[q].z, u[q].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf2f(w[e] & 0xffff);
-          acc[2 * e + 1] += bf2f(w[e] >> 16);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[slot][8 * cg + e] = acc[e];
-  __syncthreads();
-  if (tid < 64 && blockIdx.x * 64 + tid < N) {
-    float t = 0.f;
-    for (int sl = 0; sl < 32; ++sl) t += red[sl][tid];
-    part[(size_t)blockIdx.y * N + blockIdx.x * 64 + tid] = t;
-  }
-}
-
 // ------------------------------------------------------ output dropout
 // dYd[m][n] = dY[m][n] * z_mn (z = 1/(1-p) kept, 0 dropped; the c_proj
 // output mask of philox.cuh), one thread per 4 columns.

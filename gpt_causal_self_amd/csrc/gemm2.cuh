@@ -364,12 +364,49 @@ struct Epi2Partial {
   }
 };
 
+// Split-K partials that also carry the column sums of B over the slice's
+// k-range (a weight gradient's bias gradient: B is the output gradient, and
+// db[n] = sum_k B(k, n)).  With `colsum` set, the blocks of the first row
+// tile add up the B fragments their first wave row reads for the MFMAs and
+// write the sums to row M of the slice's partial block (split_stride covers
+// M + 1 rows).
+struct Epi2PartialCS {
+  float* part;
+  int ldc;
+  size_t split_stride;
+  int M;
+  int colsum;
+  static constexpr bool kColSumB = true;
+  __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
+    *reinterpret_cast<float4*>(part + (size_t)blockIdx.y * split_stride + (size_t)m * ldc + n) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  }
+  __device__ __forceinline__ void store_colsum(int n, float v) const {
+    part[(size_t)blockIdx.y * split_stride + (size_t)M * ldc + n] = v;
+  }
+};
+
+template <class Epi, class = void>
+struct ColSumB { static constexpr bool value = false; };
+template <class Epi>
+struct ColSumB<Epi, decltype(void(Epi::kColSumB))> { static constexpr bool value = Epi::kColSumB; };
+
+// Sum of the 8 bf16 values of an MFMA operand fragment, in fp32.
+__device__ __forceinline__ float frag_sum8(const bf16x8& f) {
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += (float)f[e];
+  return s;
+}
+
 // One step of the ring: issue the loads of a later k-tile into stage `wr`
 // (when `load`) and multiply the k-tile held in stage `rd` into acc.  The two
 // stages are disjoint; the restrict qualifiers tell the compiler so, and it
 // then does not make the operand reads wait for the loads just issued (the
 // caller's vmcnt wait and barrier order each stage's loads before its reads).
-template <int BM, int BN, int BK, bool A_KC, bool B_KC, int WGM, int WGN>
+// CS: also add each B fragment's 8 values into cs[j] when do_cs (the column
+// sums of B; see Epi2PartialCS).
+template <int BM, int BN, int BK, bool A_KC, bool B_KC, int WGM, int WGN, bool CS = false>
 __device__ __forceinline__ void g2_step(const char* __restrict__ rd, char* __restrict__ wr,
                                         bool load, const bf16_t* __restrict__ A, int lda,
                                         const bf16_t* __restrict__ Bm, int ldb, int m0, int n0,
@@ -377,7 +414,8 @@ __device__ __forceinline__ void g2_step(const char* __restrict__ rd, char* __res
                                         int wm, int wn,
                                         floatx16 (&acc)[BM / WGM / 32][BN / WGN / 32],
                                         const G2Off<BM, BK, A_KC, WGM * WGN>& pa,
-                                        const G2Off<BN, BK, B_KC, WGM * WGN>& pb) {
+                                        const G2Off<BN, BK, B_KC, WGM * WGN>& pb,
+                                        bool do_cs = false, float* cs = nullptr) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MT = WTM / 32, NT = WTN / 32;
@@ -393,6 +431,12 @@ __device__ __forceinline__ void g2_step(const char* __restrict__ rd, char* __res
     for (int i = 0; i < MT; ++i) af[i] = g2_frag<BM, BK, A_KC>(rd, wm * WTM + i * 32, kk, lane);
 #pragma unroll
     for (int j = 0; j < NT; ++j) bfr[j] = g2_frag<BN, BK, B_KC>(rd + kA, wn * WTN + j * 32, kk, lane);
+    if constexpr (CS) {
+      if (do_cs) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) cs[j] += frag_sum8(bfr[j]);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -608,6 +652,15 @@ void gemm2_kernel(
                                  pb);
     }
 
+  // column sums of B (Epi2PartialCS): the first wave row of the first row
+  // tile's blocks, from the B fragments it reads anyway
+  constexpr bool kCS = ColSumB<Epi>::value;
+  float cs[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) cs[j] = 0.f;
+  bool do_cs = false;
+  if constexpr (kCS) do_cs = epi.colsum && m0 == 0 && wm == 0;
+
   for (int kt = 0; kt < nk; ++kt) {
     // tile kt is complete once at most (later tiles issued) x loads remain
     const int later = min(nk - 1, kt + NSTAGE - 2) - kt;
@@ -617,9 +670,22 @@ void gemm2_kernel(
     else wait_vmcnt<0>();
     bar_nofence();
     const int kn = kt + NSTAGE - 1;
-    g2_step<BM, BN, BK, A_KC, B_KC, WGM, WGN>(
+    g2_step<BM, BN, BK, A_KC, B_KC, WGM, WGN, kCS>(
         smem + (kt % NSTAGE) * Cfg::kStage, smem + (kn % NSTAGE) * Cfg::kStage, kn < nk, A, lda,
-        Bm, ldb, m0, n0, M, N, kbeg + kn * BK, kend, wid, lane, wm, wn, acc, pa, pb);
+        Bm, ldb, m0, n0, M, N, kbeg + kn * BK, kend, wid, lane, wm, wn, acc, pa, pb, do_cs, cs);
+  }
+  if constexpr (kCS) {
+    // lanes l and l ^ 32 hold the two k halves of column l % 32 of each
+    // fragment: B fragment j of wave column wn covers columns
+    // n0 + wn * WTN + 32 j + (lane % 32)
+    if (do_cs) {
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const float v = cs[j] + __shfl_xor(cs[j], 32);
+        const int n = n0 + wn * WTN + j * 32 + lane;
+        if (lane < 32 && n < N) epi.store_colsum(n, v);
+      }
+    }
   }
 
   if constexpr (kStagedEpi) {

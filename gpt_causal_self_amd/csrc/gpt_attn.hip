@@ -261,12 +261,9 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hs));
   const size_t head_elems = (size_t)B * H * T * hs;
   float* part = h->part;                                   // split-K partials
-  float* cpart = h->part + (size_t)kWgradSplits * C * N3;  // column-sum partials
+  float* cpart = h->part + (size_t)kWgradSplits * (C + 1) * N3;  // column-sum partials
   const int rows_per = (M + kColsumSplits - 1) / kColsumSplits;
   const int ncs = rows_per > 0 ? (M + rows_per - 1) / rows_per : 0;
-  // bf16 column sums: row slices of about 384 rows (12 rows per thread)
-  const int bcs = std::max(1, std::min(kColsumSplits, (M + 383) / 384));
-  const int brows = (M + bcs - 1) / bcs;
   // Split-K factor of a weight-gradient GEMM: as many k-slices as fit the
   // chip in one pass (two 128x128 blocks per CU on 256 CUs), so no block
   // waits for a second round.
@@ -341,18 +338,18 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     // the weight and bias gradients of c_proj need only dY and o: side stream
     const hipStream_t sd = h->side;
     (void)hipStreamWaitEvent(sd, h->ev_fork, 0);
-    Epi2Partial e_wp{part, C, (size_t)C * C};
+    // db_proj = colsum(dY) comes with the GEMM (row C of each slice's
+    // partials, Epi2PartialCS) and is reduced with it
+    Epi2PartialCS e_wp{part, C, (size_t)(C + 1) * C, C, db_proj ? 1 : 0};
     const int s1 = splits_for(((C + 127) / 128) * ((C + 127) / 128));
     const int n1 = launch_gemm2<GA_WGRAD_TILE, false, false>(o, C, (const bf16_t*)dY, C, C, C, M,
                                                              e_wp, sd, s1);
     hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, sd, part, n1,
-                       (size_t)C * C, (size_t)C * C, (bf16_t*)dW_proj);
-    if (db_proj) {
-      hipLaunchKernelGGL(colsum_bf16_kernel, dim3((C + 63) / 64, bcs), dim3(256), 0, sd,
-                         (const bf16_t*)dY, M, C, C, brows, cpart);
-      hipLaunchKernelGGL(reduce_colparts_kernel<bf16_t>, dim3((C + 63) / 64), dim3(256), 0, sd,
-                         cpart, bcs, C, (bf16_t*)db_proj);
-    }
+                       (size_t)C * C, (size_t)(C + 1) * C, (bf16_t*)dW_proj);
+    if (db_proj)
+      hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(1), dim3(256), 0, sd,
+                         part + (size_t)C * C, n1, (size_t)C, (size_t)(C + 1) * C,
+                         (bf16_t*)db_proj);
     mark(h, 5, st);
     // ---- attention core
     const bf16_t* q = qkv;
@@ -397,7 +394,7 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     // ---- c_attn: dx = dqkv W_attn^T ; dW_attn = x^T dqkv ; db_attn = colsum(dqkv)
     (void)hipEventRecord(h->ev_mid, st);  // dqkv ready
     (void)hipStreamWaitEvent(sd, h->ev_mid, 0);
-    Epi2Partial e_wa{part, N3, (size_t)C * N3};
+    Epi2PartialCS e_wa{part, N3, (size_t)(C + 1) * N3, C, db_attn ? 1 : 0};
     int s2;
     {
       constexpr int tile[] = {GA_WGRAD_ATTN_TILE};
@@ -407,13 +404,11 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     const int n2 = launch_gemm2<GA_WGRAD_ATTN_TILE, false, false>(
         (const bf16_t*)x, C, dqkv, N3, C, N3, M, e_wa, sd, s2);
     hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, sd, part, n2,
-                       (size_t)C * N3, (size_t)C * N3, (bf16_t*)dW_attn);
-    if (db_attn) {
-      hipLaunchKernelGGL(colsum_bf16_kernel, dim3((N3 + 63) / 64, bcs), dim3(256), 0, sd, dqkv, M,
-                         N3, N3, brows, cpart);
-      hipLaunchKernelGGL(reduce_colparts_kernel<bf16_t>, dim3((N3 + 63) / 64), dim3(256), 0,
-                         sd, cpart, bcs, N3, (bf16_t*)db_attn);
-    }
+                       (size_t)C * N3, (size_t)(C + 1) * N3, (bf16_t*)dW_attn);
+    if (db_attn)  // colsum(dqkv): row C of the slices' partials
+      hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3((N3 + 1023) / 1024), dim3(256), 0, sd,
+                         part + (size_t)C * N3, n2, (size_t)N3, (size_t)(C + 1) * N3,
+                         (bf16_t*)db_attn);
     Epi2RowMajor e_dx{(bf16_t*)dx, C, nullptr};
     if (use_gemm3(M, C))
       launch_gemm3<GA_DGRAD3_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3,

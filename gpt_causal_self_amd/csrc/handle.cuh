@@ -138,7 +138,9 @@ Layout layout(int C, int H, int max_B, int max_T, size_t es) {
   L.dym = off;   off = align_up(off + BT * C * es);
   L.dqkv = off;  off = align_up(off + 3 * BT * C * es);
   L.delta = off; off = align_up(off + (size_t)max_B * H * max_T * sizeof(float));
-  L.part_elems = (size_t)kWgradSplits * C * 3 * C + (size_t)kColsumSplits * 3 * C;
+  // split-K partials of the weight gradients, each slice C + 1 rows (the last
+  // holds the bias gradient's column sums), then column-sum partials
+  L.part_elems = (size_t)kWgradSplits * (C + 1) * 3 * C + (size_t)kColsumSplits * 3 * C;
   L.part = off;  off = align_up(off + L.part_elems * sizeof(float));
   L.ln = off;    off = align_up(off + BT * C * es);
   L.rowstats = off;
