@@ -194,11 +194,13 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T_* __restric
 }
 
 // out[i] = sum_{s < S} part[s*stride + i] for i < n, in the output type.
-// out[i..i+3] = sum_k part[k][i..i+3] (n, stride multiples of 4; 16-byte
-// partial loads).
+// out[i..i+3] = sum_k part[k][i..i+3] (n, n2, stride multiples of 4; 16-byte
+// partial loads).  The n2 elements after the first n of each slice (a
+// weight gradient's bias row) go to out2 in the same pass.
 __global__ __launch_bounds__(256) void reduce_partials4_bf16_kernel(
-    const float* __restrict__ part, int S, size_t n, size_t stride, bf16_t* __restrict__ out) {
-  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n;
+    const float* __restrict__ part, int S, size_t n, size_t stride, bf16_t* __restrict__ out,
+    size_t n2, bf16_t* __restrict__ out2) {
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n + n2;
        i += (size_t)gridDim.x * 256 * 4) {
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int k = 0; k < S; ++k) {
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(256) void reduce_partials4_bf16_kernel(
     uint2 w;
     w.x = pack_bf16x2(s.x, s.y);
     w.y = pack_bf16x2(s.z, s.w);
-    *reinterpret_cast<uint2*>(out + i) = w;
+    *reinterpret_cast<uint2*>(i < n ? out + i : out2 + (i - n)) = w;
   }
 }
 

@@ -33,13 +33,23 @@ constexpr int kG3Loaders = 2;  // waves 0 and 4
 constexpr int kG3Waves = 8;
 
 // Chunk slot <-> source chunk of a row-contiguous tile with CPR 16-byte
-// chunks per k-row (an involution; XOR by 0, 4, 8 or 12 stays inside the
-// aligned group of 16 chunks, so chunks past the last full group keep their
-// place).
+// chunks per k-row (an involution).  A transposing fragment read takes 4
+// consecutive k-rows at the same columns; LDS has 64 four-byte banks, so a
+// k-row of CPR chunks starts 4 CPR banks after the previous one.  When that is
+// a multiple of 64 (CPR % 16 == 0) the 4 rows would hit the same banks and
+// XOR by 0, 4, 8 or 12 chunks (64-byte steps, inside the aligned group of 16)
+// spreads them; when it is 16 or 48 banks (CPR % 16 == 4 or 12, e.g. 288
+// columns) the rows already fall 16 banks apart and a swizzle would put two of
+// them back together; in the remaining cases the XOR goes over the chunks
+// below the last multiple of 16.
 template <int CPR>
 __device__ __forceinline__ int rc_swz(int chunk, int krow) {
-  constexpr int kFull = CPR & ~15;
-  return chunk < kFull ? (chunk ^ ((krow & 3) << 2)) : chunk;
+  if constexpr (CPR % 16 == 4 || CPR % 16 == 12) {
+    return chunk;
+  } else {
+    constexpr int kFull = CPR & ~15;
+    return chunk < kFull ? (chunk ^ ((krow & 3) << 2)) : chunk;
+  }
 }
 
 // Per-lane source offsets (elements, at k0 = 0) of the 1 KB loads that
@@ -170,8 +180,9 @@ __global__ __launch_bounds__(64 * kG3Waves) void gemm3_kernel(const bf16_t* __re
                                                               int ldb, int M, int N, int K,
                                                               Epi epi) {
   static_assert(WGM * WGN == kG3Waves - kG3Loaders, "six MFMA waves");
-  static_assert(Staged<Epi>::value && !Store8All<Epi>::value, "staged epilogues");
+  static_assert(Staged<Epi>::value, "staged epilogues");
   constexpr bool kF32 = StagedF32<Epi>::value;
+  static_assert(!(kF32 && Store8All<Epi>::value), "store8_all goes with the bf16 staging");
   static_assert(!kF32 || WGM == 1, "fp32 staging goes by 32-row blocks of a one-row wave grid");
   static_assert(BK == 64 || BK == 32, "BK");
   static_assert(B_KC || (BN / 8) % 2 == 0, "row-contiguous tile");
@@ -334,10 +345,33 @@ __global__ __launch_bounds__(64 * kG3Waves) void gemm3_kernel(const bf16_t* __re
   if constexpr (!kF32) {
     bar_after_lds_writes();
     constexpr int kChunks = BM * BN / 8;
-    for (int c = tid; c < kChunks; c += 64 * kG3Waves) {
-      const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
-      const int m = m0 + rl, n = n0 + cl;
-      if (m < M && n < N) epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
+    if constexpr (Store8All<Epi>::value) {
+      // every lane in every pass (the epilogue combines lanes); the
+      // epilogue's own operands of all passes are loaded before the first
+      // store, which later loads would wait behind (they may alias)
+      static_assert(kChunks % (64 * kG3Waves) == 0, "store8_all needs every lane in every pass");
+      constexpr int kPass = kChunks / (64 * kG3Waves);
+      typename Epi::Extra ex[kPass];
+#pragma unroll
+      for (int p = 0; p < kPass; ++p) {
+        const int c = tid + p * 64 * kG3Waves;
+        const int m = m0 + c / (BN / 8), n = n0 + (c % (BN / 8)) * 8;
+        ex[p] = epi.extra(m, n, m < M && n < N);
+      }
+#pragma unroll
+      for (int p = 0; p < kPass; ++p) {
+        const int c = tid + p * 64 * kG3Waves;
+        const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+        const int m = m0 + rl, n = n0 + cl;
+        epi.store8_all(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl),
+                       m < M && n < N, lane, ex[p]);
+      }
+    } else {
+      for (int c = tid; c < kChunks; c += 64 * kG3Waves) {
+        const int rl = c / (BN / 8), cl = (c % (BN / 8)) * 8;
+        const int m = m0 + rl, n = n0 + cl;
+        if (m < M && n < N) epi.store8(m, n, *reinterpret_cast<const uint4*>(ct + rl * SP + cl));
+      }
     }
   }
 }

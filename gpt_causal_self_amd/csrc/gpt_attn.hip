@@ -88,11 +88,9 @@ int gpt_attn_create(gpt_attn_t* out, int C, int n_head, int max_B, int max_T, in
     return GPT_ATTN_ERR_HIP;
   }
   if (hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_mid, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
     (void)hipGetLastError();
     if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
-    if (h->ev_mid) (void)hipEventDestroy(h->ev_mid);
     (void)hipStreamDestroy(h->side);
     (void)hipFree(ws);
     free(h);
@@ -112,7 +110,6 @@ int gpt_attn_destroy(gpt_attn_t h) {
   }
   if (h->keepq && hipFree(h->keepq) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   if (h->ev_fork && hipEventDestroy(h->ev_fork) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
-  if (h->ev_mid && hipEventDestroy(h->ev_mid) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   if (h->ev_join && hipEventDestroy(h->ev_join) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   if (h->side && hipStreamDestroy(h->side) != hipSuccess) rc = GPT_ATTN_ERR_HIP;
   free(h);
@@ -317,24 +314,31 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
                          0, st, (const bf16_t*)dY, (bf16_t*)h->ln, (long)M, C, dp);
       dY = h->ln;
     }
-    // Weight and bias gradients go to the handle's side stream, forked here
-    // (dY and o ready) and joined back into st at the end; the split-K and
-    // column-sum partials are used on the side stream only.
+    // The c_proj weight and bias gradients go to the handle's side stream,
+    // forked here (dY and o ready), where they run beside the dO product and
+    // the attention backward; the side stream is joined back into st once
+    // dqkv is ready, before the c_attn weight gradient reuses the split-K
+    // partials (which carry the bias column sums).  Running the c_attn
+    // weight gradient on the side stream too, beside the dx product, gained
+    // nothing over running the two in sequence and cost one more fork.
     (void)hipEventRecord(h->ev_fork, st);
     // ---- c_proj: dym = dY W_proj^T (its epilogue also writes the softmax
     // backward row statistics D and L) ; dW_proj = ym^T dY ; db_proj = colsum(dY)
     const int Tpad = (T + 63) / 64 * 64;
     float* Dpad = h->rowstats;
     float* Lpad = h->rowstats + (size_t)B * H * Tpad;
-    if (hs == 64) {
-      Epi2DgradRowStats<64> e_dym{dym, C, nullptr, o, h->lse, Dpad, Lpad, T, H, Tpad};
-      launch_gemm2<GA_DGRAD_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M,
-                                              C, C, e_dym, st);
-    } else {
-      Epi2DgradRowStats<32> e_dym{dym, C, nullptr, o, h->lse, Dpad, Lpad, T, H, Tpad};
-      launch_gemm2<GA_DGRAD_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C, M,
-                                              C, C, e_dym, st);
-    }
+    auto dgrad_rowstats = [&](auto e_dym) {
+      if (use_gemm3(M, C))
+        launch_gemm3<GA_DGRAD3_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C,
+                                                 M, C, C, e_dym, st);
+      else
+        launch_gemm2<GA_DGRAD_TILE, true, true>((const bf16_t*)dY, C, (const bf16_t*)W_proj, C,
+                                                M, C, C, e_dym, st);
+    };
+    if (hs == 64)
+      dgrad_rowstats(Epi2DgradRowStats<64>{dym, C, nullptr, o, h->lse, Dpad, Lpad, T, H, Tpad});
+    else
+      dgrad_rowstats(Epi2DgradRowStats<32>{dym, C, nullptr, o, h->lse, Dpad, Lpad, T, H, Tpad});
     // the weight and bias gradients of c_proj need only dY and o: side stream
     const hipStream_t sd = h->side;
     (void)hipStreamWaitEvent(sd, h->ev_fork, 0);
@@ -345,11 +349,9 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     const int n1 = launch_gemm2<GA_WGRAD_TILE, false, false>(o, C, (const bf16_t*)dY, C, C, C, M,
                                                              e_wp, sd, s1);
     hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, sd, part, n1,
-                       (size_t)C * C, (size_t)(C + 1) * C, (bf16_t*)dW_proj);
-    if (db_proj)
-      hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(1), dim3(256), 0, sd,
-                         part + (size_t)C * C, n1, (size_t)C, (size_t)(C + 1) * C,
-                         (bf16_t*)db_proj);
+                       (size_t)C * C, (size_t)(C + 1) * C, (bf16_t*)dW_proj,
+                       db_proj ? (size_t)C : 0, (bf16_t*)db_proj);
+    (void)hipEventRecord(h->ev_join, sd);
     mark(h, 5, st);
     // ---- attention core
     const bf16_t* q = qkv;
@@ -392,8 +394,14 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
     }
     mark(h, 6, st);
     // ---- c_attn: dx = dqkv W_attn^T ; dW_attn = x^T dqkv ; db_attn = colsum(dqkv)
-    (void)hipEventRecord(h->ev_mid, st);  // dqkv ready
-    (void)hipStreamWaitEvent(sd, h->ev_mid, 0);
+    (void)hipStreamWaitEvent(st, h->ev_join, 0);
+    Epi2RowMajor e_dx{(bf16_t*)dx, C, nullptr};
+    if (use_gemm3(M, C))
+      launch_gemm3<GA_DGRAD3_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3,
+                                               e_dx, st);
+    else
+      launch_gemm2<GA_DGRAD_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3,
+                                              e_dx, st);
     Epi2PartialCS e_wa{part, N3, (size_t)(C + 1) * N3, C, db_attn ? 1 : 0};
     int s2;
     {
@@ -402,22 +410,11 @@ int gpt_attn_backward(gpt_attn_t h, const void* x, const void* W_attn, const voi
       s2 = std::max(1, std::min(kWgradSplits, 256 * GA_WGRAD_ATTN_PER_CU / tiles));
     }
     const int n2 = launch_gemm2<GA_WGRAD_ATTN_TILE, false, false>(
-        (const bf16_t*)x, C, dqkv, N3, C, N3, M, e_wa, sd, s2);
-    hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, sd, part, n2,
-                       (size_t)C * N3, (size_t)(C + 1) * N3, (bf16_t*)dW_attn);
-    if (db_attn)  // colsum(dqkv): row C of the slices' partials
-      hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3((N3 + 1023) / 1024), dim3(256), 0, sd,
-                         part + (size_t)C * N3, n2, (size_t)N3, (size_t)(C + 1) * N3,
-                         (bf16_t*)db_attn);
-    Epi2RowMajor e_dx{(bf16_t*)dx, C, nullptr};
-    if (use_gemm3(M, C))
-      launch_gemm3<GA_DGRAD3_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3,
-                                               e_dx, st);
-    else
-      launch_gemm2<GA_DGRAD_TILE, true, true>(dqkv, N3, (const bf16_t*)W_attn, N3, M, C, N3,
-                                              e_dx, st);
-    (void)hipEventRecord(h->ev_join, sd);
-    (void)hipStreamWaitEvent(st, h->ev_join, 0);
+        (const bf16_t*)x, C, dqkv, N3, C, N3, M, e_wa, st, s2);
+    // db_attn = colsum(dqkv): row C of the slices' partials, reduced with them
+    hipLaunchKernelGGL(reduce_partials4_bf16_kernel, dim3(rblocks), dim3(256), 0, st, part, n2,
+                       (size_t)C * N3, (size_t)(C + 1) * N3, (bf16_t*)dW_attn,
+                       db_attn ? (size_t)N3 : 0, (bf16_t*)db_attn);
   } else {
     const float* qkv = (const float*)h->qkv;
     const float* o = (const float*)h->o;

@@ -96,10 +96,11 @@ struct gpt_attn_handle {
   hipEvent_t ev[8];
   int n_ev;
   // second stream of the backward (default priority, non-blocking): the
-  // weight and bias gradients run there beside the data-gradient chain,
-  // forked from and joined back into the caller's stream by these events
+  // c_proj weight and bias gradients run there beside the data-gradient
+  // chain, forked from and joined back into the caller's stream by these
+  // events
   hipStream_t side;
-  hipEvent_t ev_fork, ev_mid, ev_join;
+  hipEvent_t ev_fork, ev_join;
 };
 
 namespace {
