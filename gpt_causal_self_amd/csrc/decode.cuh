@@ -123,30 +123,30 @@ __global__ __launch_bounds__(64 * kDecWaves) void skinny_gemm_kernel(
 // Attention of one query per (b, h) over cached keys [chunk * CHUNK,
 // min(pos + 1, (chunk + 1) * CHUNK)), CHUNK = KPW keys per wave of the NT
 // threads.  Each wave takes KPW consecutive keys and runs on its own as its
-// loads arrive: lane l scores keys l, l + 64, ..., the wave takes its max,
-// exp2 weights and sum, passes the weights through its own LDS slice, and
-// for the weighted value sum lane l takes 8 value columns (dg) of a group of
-// consecutive keys (kg); the groups are summed with lane shuffles.  The
-// waves' (m, l, o) then merge after the block's one barrier, each rescaled
-// to the common maximum.  More, shorter waves per block keep more of the
-// cache's loads in flight on the block's CU (16 waves of 64 keys: a 1024-key
-// cache in one block).  One
-// chunk: the block writes y_m[b][h*HS + d] = bf16(o / l).  Several: it writes
-// (m, l, o[0..HS)) in fp32 (m the chunk's max of the log2-scaled scores,
-// l = sum 2^(s - m), o = sum 2^(s - m) v), and the last chunk block of the
-// (b, h) to finish merges the chunks the same way.
+// loads arrive.  Lane l holds 8 columns (dg = l % (HS/8)) of the key and
+// value rows of a group of consecutive keys (kg = l / (HS/8)), so every load
+// instruction reads whole 128-byte rows (a lane per 16-byte chunk) for both
+// caches.  A key's score is the sum of its group's HS/8 partial dot products
+// (lane shuffles inside the group, after which every lane of the group holds
+// the group's scores); the wave's max and sum and the weighted value sum are
+// then taken over the groups.  The waves' (m, l, o) merge after the block's
+// one barrier, each rescaled to the common maximum.  More, shorter waves per
+// block keep more of the cache's loads in flight on the block's CU (16 waves
+// of 64 keys: a 1024-key cache in one block).  One chunk: the block writes
+// y_m[b][h*HS + d] = bf16(o / l).  Several: it writes (m, l, o[0..HS)) in
+// fp32 (m the chunk's max of the log2-scaled scores, l = sum 2^(s - m),
+// o = sum 2^(s - m) v), and the last chunk block of the (b, h) to finish
+// merges the chunks the same way.
 template <int HS, int NT, int KPW>
 __global__ __launch_bounds__(NT) void decode_attn_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, float* __restrict__ part, bf16_t* __restrict__ ym, int H,
     int cache_T, int pos, int nchunk, float scale_log2, unsigned* __restrict__ counters) {
-  static_assert(KPW % 64 == 0, "a lane per key, KPW / 64 keys each");
   constexpr int NW = NT / 64;
-  constexpr int KT = KPW / 64;              // keys per lane for the scores
   constexpr int CHUNK = NW * KPW;           // keys per block
-  constexpr int DG = HS / 8, KG = 64 / DG;  // value columns / key groups per wave
+  constexpr int DG = HS / 8, KG = 64 / DG;  // column chunks of a row / key groups per wave
   constexpr int KPG = KPW / KG;             // keys per group
-  __shared__ float ps[NW][KPW];
+  static_assert(KPW % KG == 0, "whole key groups per wave");
   __shared__ float wpart[NW][HS + 2];
   __shared__ int is_last;
   const int bh = blockIdx.x, chunk = blockIdx.y;
@@ -156,61 +156,60 @@ __global__ __launch_bounds__(NT) void decode_attn_kernel(
   const size_t head = ((size_t)b * H + h) * cache_T * HS;
   const int kw0 = chunk * CHUNK + w * KPW;  // this wave's first key
   const int dg = lane % DG, kg = lane / DG;
-  const int jb = kw0 + kg * KPG;
-  uint4 vr[KPG];
+  const int jb = kw0 + kg * KPG;            // this group's first key
+  uint4 kr[KPG], vr[KPG];
+#pragma unroll
+  for (int u = 0; u < KPG; ++u)
+    kr[u] = jb + u <= pos
+                ? *reinterpret_cast<const uint4*>(k_cache + head + (size_t)(jb + u) * HS + 8 * dg)
+                : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
   for (int u = 0; u < KPG; ++u)
     vr[u] = jb + u <= pos
                 ? *reinterpret_cast<const uint4*>(v_cache + head + (size_t)(jb + u) * HS + 8 * dg)
                 : make_uint4(0u, 0u, 0u, 0u);
-  uint4 kr[KT][HS / 8];
+  float qf[8];
+  {
+    const uint4 uq = *reinterpret_cast<const uint4*>(q + (size_t)b * C + h * HS + 8 * dg);
+    const unsigned wq[4] = {uq.x, uq.y, uq.z, uq.w};
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    const int j = kw0 + lane + 64 * t;
-#pragma unroll
-    for (int d8 = 0; d8 < HS / 8; ++d8)
-      kr[t][d8] = j <= pos
-                      ? *reinterpret_cast<const uint4*>(k_cache + head + (size_t)j * HS + 8 * d8)
-                      : make_uint4(0u, 0u, 0u, 0u);
+    for (int e = 0; e < 4; ++e) {
+      qf[2 * e] = bf2f(wq[e] & 0xffff);
+      qf[2 * e + 1] = bf2f(wq[e] >> 16);
+    }
   }
-  float s[KT];
-  float m = -INFINITY;
+  // partial dot products over this lane's 8 columns, summed over the group
+  float s[KPG];
 #pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    const int j = kw0 + lane + 64 * t;
+  for (int u = 0; u < KPG; ++u) {
+    const unsigned wd[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
     float acc = 0.f;
 #pragma unroll
-    for (int d8 = 0; d8 < HS / 8; ++d8) {
-      const uint4 uq = *reinterpret_cast<const uint4*>(q + (size_t)b * C + h * HS + 8 * d8);
-      const unsigned wq[4] = {uq.x, uq.y, uq.z, uq.w};
-      const unsigned wd[4] = {kr[t][d8].x, kr[t][d8].y, kr[t][d8].z, kr[t][d8].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(bf2f(wq[e] & 0xffff), bf2f(wd[e] & 0xffff), acc);
-        acc = fmaf(bf2f(wq[e] >> 16), bf2f(wd[e] >> 16), acc);
-      }
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(qf[2 * e], bf2f(wd[e] & 0xffff), acc);
+      acc = fmaf(qf[2 * e + 1], bf2f(wd[e] >> 16), acc);
     }
-    s[t] = j <= pos ? acc * scale_log2 : -INFINITY;
-    m = fmaxf(m, s[t]);
+    s[u] = acc;
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  for (int o = 1; o < DG; o <<= 1)
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) s[u] += __shfl_xor(s[u], o);
+  float m = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < KPG; ++u) {
+    s[u] = jb + u <= pos ? s[u] * scale_log2 : -INFINITY;
+    m = fmaxf(m, s[u]);
+  }
+#pragma unroll
+  for (int o = DG; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
   // weights of keys past pos are 0 (also when the whole wave is past pos)
   float l = 0.f;
-#pragma unroll
-  for (int t = 0; t < KT; ++t) {
-    const float p = kw0 + lane + 64 * t <= pos ? __builtin_amdgcn_exp2f(s[t] - m) : 0.f;
-    ps[w][lane + 64 * t] = p;
-    l += p;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-  // the wave's weights are read back by other lanes of the same wave
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   float o8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < KPG; ++u) {
-    const float pj = ps[w][kg * KPG + u];
+    const float pj = jb + u <= pos ? __builtin_amdgcn_exp2f(s[u] - m) : 0.f;
+    l += pj;
     const unsigned wd[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -220,9 +219,11 @@ __global__ __launch_bounds__(NT) void decode_attn_kernel(
   }
   // sum the key groups: lanes dg, dg + DG, ... hold the same columns
 #pragma unroll
-  for (int o = DG; o < 64; o <<= 1)
+  for (int o = DG; o < 64; o <<= 1) {
+    l += __shfl_xor(l, o);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o8[e] += __shfl_xor(o8[e], o);
+  }
   if (kg == 0) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) wpart[w][2 + 8 * dg + e] = o8[e];
