@@ -86,6 +86,12 @@ def test_backward_training_step_workload_full():
               f"normwise vs exact {rel:.2e}", flush=True)
 
 
+def test_backward_long_sequence():
+    """One sequence of 2500 positions (key and query chains of 40 tiles, a
+    ragged last tile): every gradient against the fp64 oracle."""
+    check_grads(make_inputs(1, 2500, 768, 12, dtype="bf16", seed=2500, with_dY=True))
+
+
 def test_backward_ragged_rows_wide_projection():
     """B*T = 6600 rows at C = 768: the dx product runs on 96 x 384 tiles
     (138 of them, the last row tile 72 rows deep), every gradient against the

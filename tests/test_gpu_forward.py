@@ -69,6 +69,14 @@ def test_ragged_rows_wide_projection():
     _check(inp, batches=(5, 7))
 
 
+@pytest.mark.parametrize("T", [4096, 2999])
+def test_long_sequence(T):
+    """One sequence four times the workloads' block size (32 query tiles of
+    128, key chains of up to 64 tiles), and a ragged length past 2048;
+    every stage against the oracle."""
+    _check(make_inputs(1, T, 768, 12, dtype="bf16", seed=T))
+
+
 @pytest.mark.parametrize("T", WORKLOADS[4].ragged_T)
 def test_workload_gpt2_xl_ragged(T):
     """Every sequence of each prefix length, stages included."""
