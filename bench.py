@@ -344,7 +344,7 @@ def write_kernel_stats(stats_dir, out_md):
     if traces:
         B, T, C, H = 12, 1024, 768, 12
         M = B * T
-        want = {"c_attn": ("Epi2QKV", (M // 256) * (3 * C // 256) * 512, 1),
+        want = {"c_attn": ("Epi2QKV", (M // 256) * (3 * C // 256) * 1024, 1),
                 "attention": ("attn_fwd2_bf16_kernel<64, 2, false>", B * H * 256, T // 128),
                 "c_proj": ("gemm3_kernel<96, 384, 32, 4, true, false, 1, 6, "
                            "gpt_attn::Epi2RowMajor>", ((M + 95) // 96) * (C // 384) * 512, 1)}

@@ -12,8 +12,14 @@
 
 // Tile shapes (BM, BN, pipeline stages, BK, wave grid rows, wave grid columns)
 // of the bf16 GEMMs.
+// c_attn: 256 x 256 tiles over 16 waves (4 x 4 grid of 64 x 64 wave tiles,
+// 126 VGPRs), so each SIMD holds four waves of the block instead of two and
+// the operand loads of some waves are issued while others multiply
 #ifndef GA_QKV_TILE
-#define GA_QKV_TILE 256, 256, 2, 64, 2, 4
+#define GA_QKV_TILE 256, 256, 2, 64, 4, 4
+#endif
+#ifndef GA_QKV_OCC
+#define GA_QKV_OCC 4
 #endif
 #ifndef GA_PROJ_TILE
 #define GA_PROJ_TILE 192, 256, 2, 64, 2, 4

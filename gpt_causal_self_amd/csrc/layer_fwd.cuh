@@ -251,7 +251,7 @@ inline void layer_forward_bf16(const gpt_attn_handle* h, const bf16_t* x, int B,
   bf16_t* o = (bf16_t*)h->o;
   Epi2QKV e1{qkv, b_attn, B, T, C, H, hs};
   mark(h, 0, st);
-  launch_proj<GA_QKV_TILE, true, false>(h, x, C, W_attn, 3 * C, M, 3 * C, C, e1, st);
+  launch_proj<GA_QKV_TILE, true, false, GA_QKV_OCC>(h, x, C, W_attn, 3 * C, M, 3 * C, C, e1, st);
   mark(h, 1, st);
   const dim3 agrid(B * H, (T + kAttnBQ - 1) / kAttnBQ);
   if (drop) {
