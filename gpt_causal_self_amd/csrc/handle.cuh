@@ -45,9 +45,10 @@
 #endif
 // weight gradient of c_attn (C x 3C over all B*T rows): 256 x 128 tiles split
 // along the rows to about one block per CU (4 slices at C = 768: half the
-// fp32 partials that 256 x 256 tiles in 8 slices leave for the reduction)
+// fp32 partials that 256 x 256 tiles in 8 slices leave for the reduction),
+// 16 waves of 64 x 32 (four waves per SIMD, as c_attn)
 #ifndef GA_WGRAD_ATTN_TILE
-#define GA_WGRAD_ATTN_TILE 256, 128, 2, 64, 4, 2
+#define GA_WGRAD_ATTN_TILE 256, 128, 2, 64, 4, 4
 #endif
 #ifndef GA_WGRAD_ATTN_PER_CU
 #define GA_WGRAD_ATTN_PER_CU 1
