@@ -53,10 +53,10 @@
 #ifndef GA_WGRAD_ATTN_PER_CU
 #define GA_WGRAD_ATTN_PER_CU 1
 #endif
-// MLP: c_fc [C -> 4C] with the GELU epilogue, c_proj [4C -> C] (waves per
-// SIMD as the last value).
+// MLP: c_fc [C -> 4C] with the GELU epilogue (12 waves of 64 x 96, three per
+// SIMD), c_proj [4C -> C] (waves per SIMD as the last value).
 #ifndef GA_FC_TILE
-#define GA_FC_TILE 192, 384, 2, 64, 2, 4, true, false, 1
+#define GA_FC_TILE 192, 384, 2, 64, 3, 4, true, false, 1
 #endif
 #ifndef GA_FCPROJ_TILE
 #define GA_FCPROJ_TILE 192, 256, 2, 64, 2, 4, true, false, 1
