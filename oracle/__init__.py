@@ -65,6 +65,8 @@ def _declare(lib):
     lib.oracle_philox4x32_10.argtypes = [u32p, u32p, u32p]
     lib.oracle_dropout_threshold.restype = ctypes.c_uint32
     lib.oracle_dropout_threshold.argtypes = [ctypes.c_double]
+    lib.oracle_dropout_threshold16.restype = ctypes.c_uint32
+    lib.oracle_dropout_threshold16.argtypes = [ctypes.c_double]
     lib.oracle_dropout_keep_attn.restype = i
     lib.oracle_dropout_keep_attn.argtypes = [i, i, i, i, i, ctypes.c_uint64, ctypes.c_uint32]
     lib.oracle_dropout_keep_resid.restype = i
@@ -279,13 +281,19 @@ def philox4x32_10(ctr, key, *, lib=None):
 
 
 def dropout_threshold(p, *, lib=None):
+    """Drop threshold of a 32-bit word (c_proj output stream)."""
     return int((lib or load()).oracle_dropout_threshold(float(p)))
+
+
+def dropout_threshold16(p, *, lib=None):
+    """Drop threshold of a 16-bit value (attention-weight stream)."""
+    return int((lib or load()).oracle_dropout_threshold16(float(p)))
 
 
 def dropout_keep_attn(b, h, H, i, j, p, seed, *, lib=None):
     lib = lib or load()
     return bool(lib.oracle_dropout_keep_attn(b, h, H, i, j, int(seed),
-                                             lib.oracle_dropout_threshold(float(p))))
+                                             lib.oracle_dropout_threshold16(float(p))))
 
 
 def dropout_keep_resid(m, n, p, seed, *, lib=None):

@@ -52,10 +52,12 @@
  * Dropout (training; nn.Dropout on the attention weights after the softmax
  * and on the c_proj output, page "nanoGPT architecture explained step by
  * step", section 3, attn_dropout / resid_dropout; rate config.dropout) is
- * available as a separate entry point.  Each element keeps or drops on a
- * 32-bit word of the Philox4x32-10 counter-based generator (Salmon, Moraes,
- * Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011):
- * dropped iff word < floor(p * 2^32); kept values are scaled by 1/(1-p).
+ * available as a separate entry point.  Each element keeps or drops on bits
+ * of the Philox4x32-10 counter-based generator (Salmon, Moraes, Dror, Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011): an attention
+ * weight on a 16-bit half of a word (dropped iff below floor(p * 2^16)), a
+ * c_proj output element on a 32-bit word (dropped iff below
+ * floor(p * 2^32)); kept values are scaled by 1/(1-p).
  *
  * Everything is double precision; callers pass the exact values the GPU
  * receives (bf16 and fp32 upcast exactly).  Work is split over threads by
@@ -367,8 +369,9 @@ typedef struct {
   int scale32;    /* keep factor held in single precision */
 } attn_bwd_ctx;
 
-int oracle_dropout_keep_attn(int b, int h, int H, int i, int j, uint64_t seed, uint32_t thresh);
+int oracle_dropout_keep_attn(int b, int h, int H, int i, int j, uint64_t seed, uint32_t thresh16);
 uint32_t oracle_dropout_threshold(double p);
+uint32_t oracle_dropout_threshold16(double p);
 
 static void attn_bwd_head(void *vctx, long item, double *scratch) {
   const attn_bwd_ctx *c = (const attn_bwd_ctx *)vctx;
@@ -381,7 +384,7 @@ static void attn_bwd_head(void *vctx, long item, double *scratch) {
   /* dropout: weight p_ij enters o_i as p_ij z_ij with z_ij = 1/(1-p) if
    * kept, 0 if dropped (z = 1 without dropout) */
   const double keep_scale = c->p > 0.0 ? keep_scale_of(c->p, c->scale32) : 1.0;
-  const uint32_t thresh = c->p > 0.0 ? oracle_dropout_threshold(c->p) : 0u;
+  const uint32_t thresh = c->p > 0.0 ? oracle_dropout_threshold16(c->p) : 0u;
   /* zero this head's dq, dk, dv columns */
   for (int t = 0; t < T; ++t) {
     double *r = c->dqkv + ((size_t)b * T + t) * ld + (size_t)h * hs;
@@ -683,6 +686,13 @@ uint32_t oracle_dropout_threshold(double p) {
   return t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
 }
 
+/* The same for a 16-bit value u: dropped iff u < t16, t16 = floor(p * 2^16)
+ * (capped at 2^16 - 1), so P(drop) = t16 / 2^16, within 2^-16 of p. */
+uint32_t oracle_dropout_threshold16(double p) {
+  const double t = floor(p * 65536.0);
+  return t >= 65535.0 ? 0xFFFFu : (uint32_t)t;
+}
+
 /* Keep decision of one element: the word (c0 & 3) of Philox(ctr = {c0 >> 2,
  * c1, c2, stream}, key = seed split into low / high 32 bits). */
 static int keep_elem(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t stream, uint64_t seed,
@@ -694,11 +704,19 @@ static int keep_elem(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t stream, uin
   return w[c0 & 3] >= thresh;
 }
 
-/* Keep mask of the attention weights of head (b, h), query i, key j:
- * stream 1, counter words (j, i, b*H + h); of the c_proj output element
- * (row m = b*T + t, column n): stream 2, counter words (n, m, 0). */
-int oracle_dropout_keep_attn(int b, int h, int H, int i, int j, uint64_t seed, uint32_t thresh) {
-  return keep_elem((uint32_t)j, (uint32_t)i, (uint32_t)(b * H + h), 1u, seed, thresh);
+/* Keep mask of the attention weights of head (b, h), query i, key j
+ * (stream 1): one Philox call covers the eight keys of the aligned group
+ * j / 8, counter {j / 8, i, b*H + h, 1}; key j takes the low (j even) or high
+ * (j odd) 16-bit half of word (j % 8) / 2 and is dropped iff that value is
+ * below thresh16.  Of the c_proj output element (row m = b*T + t, column n):
+ * stream 2, keep_elem over counter words (n, m, 0). */
+int oracle_dropout_keep_attn(int b, int h, int H, int i, int j, uint64_t seed, uint32_t thresh16) {
+  const uint32_t ctr[4] = {(uint32_t)j >> 3, (uint32_t)i, (uint32_t)(b * H + h), 1u};
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t w[4];
+  oracle_philox4x32_10(ctr, key, w);
+  const uint32_t u = (w[(j & 7) >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+  return u >= thresh16;
 }
 int oracle_dropout_keep_resid(long m, int n, uint64_t seed, uint32_t thresh) {
   return keep_elem((uint32_t)n, (uint32_t)m, 0u, 2u, seed, thresh);
@@ -710,7 +728,7 @@ typedef struct {
   double *ym;
   double p;
   uint64_t seed;
-  uint32_t thresh;
+  uint32_t thresh16; /* attention-weight drop threshold (16-bit values) */
   int round_p; /* as attn_ctx.round_p */
   int scale32; /* keep factor held in single precision */
 } drop_attn_ctx;
@@ -734,7 +752,7 @@ static void drop_attn_head(void *vctx, long item, double *p) {
     double *o = c->ym + ((size_t)b * T + i) * C + (size_t)h * hs;
     for (int d = 0; d < hs; ++d) o[d] = 0.0;
     for (int j = 0; j <= i; ++j) {
-      if (!oracle_dropout_keep_attn(b, h, H, i, j, c->seed, c->thresh)) continue;
+      if (!oracle_dropout_keep_attn(b, h, H, i, j, c->seed, c->thresh16)) continue;
       const double w = wp[j] * keep_scale;
       const double *v = c->qkv + ((size_t)b * T + j) * ld + 2 * (size_t)C + (size_t)h * hs;
       for (int d = 0; d < hs; ++d) o[d] += w * v[d];
@@ -758,9 +776,8 @@ static int forward_dropout_impl(int B, int T, int C, int H, const double *x,
   if (linear((int)M, C, 3 * C, x, W_attn, b_attn, qkv, nthreads)) return -1;
   if (store_bf16 & 1) round_all(qkv, (size_t)M * 3 * C);
   {
-    drop_attn_ctx a = {B,      T,      C,                       H,
-                       qkv,    ym,     p,                       seed,
-                       thresh, (store_bf16 & 32) != 0, (store_bf16 & 512) != 0};
+    drop_attn_ctx a = {B,   T,  C, H, qkv, ym, p, seed, oracle_dropout_threshold16(p),
+                       (store_bf16 & 32) != 0, (store_bf16 & 512) != 0};
     if (parallel_for((long)B * H, nthreads, drop_attn_head, &a, (size_t)2 * T)) return -1;
   }
   if (store_bf16 & 2) round_all(ym, (size_t)M * C);

@@ -36,6 +36,31 @@ def test_threshold():
     assert oracle.dropout_threshold(0.5) == 1 << 31
     assert oracle.dropout_threshold(0.1) == 429496729          # floor(0.1 * 2^32)
     assert oracle.dropout_threshold(0.9999999999999999) == 0xFFFFFFFF
+    assert oracle.dropout_threshold16(0.0) == 0
+    assert oracle.dropout_threshold16(0.5) == 1 << 15
+    assert oracle.dropout_threshold16(0.1) == 6553                # floor(0.1 * 2^16)
+    assert oracle.dropout_threshold16(0.9999999999999999) == 0xFFFF
+
+
+def test_element_to_counter_mapping():
+    """An attention weight (query i, key j) takes the 16-bit half j % 2 of
+    word (j % 8) / 2 of Philox({j / 8, i, b*H + h, 1}); a c_proj output element
+    (m, n) word n % 4 of Philox({n / 4, m, 0, 2}).  Checked against the
+    pinned generator, keys of one group against each other, for a rate at
+    which both outcomes are common."""
+    p, seed = 0.5, (5 << 32) | 77
+    key = [77, 5]
+    t16, t32 = oracle.dropout_threshold16(p), oracle.dropout_threshold(p)
+    b, h, H = 1, 2, 4
+    for i in (0, 3, 9, 130):
+        for j in range(0, 24):
+            w = oracle.philox4x32_10([j >> 3, i, b * H + h, 1], key)
+            u = (w[(j & 7) >> 1] >> (16 * (j & 1))) & 0xFFFF
+            assert oracle.dropout_keep_attn(b, h, H, i, j, p, seed) == (u >= t16), (i, j)
+    for m in (0, 7, 1025):
+        for n in range(0, 12):
+            w = oracle.philox4x32_10([n >> 2, m, 0, 2], key)[n & 3]
+            assert oracle.dropout_keep_resid(m, n, p, seed) == (w >= t32), (m, n)
 
 
 def test_keep_rate_and_independence():

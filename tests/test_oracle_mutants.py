@@ -75,6 +75,9 @@ MUTANTS = [
     ("residual dropout not rescaled", [("? y[(size_t)m * C + n] * keep_scale",
                                         "? y[(size_t)m * C + n]", 0)]),
     ("dropout word index", [("return w[c0 & 3] >= thresh;", "return w[0] >= thresh;", 0)]),
+    ("attention dropout half", [("(w[(j & 7) >> 1] >> (16 * (j & 1))) & 0xFFFFu",
+                                 "(w[(j & 7) >> 1]) & 0xFFFFu", 0)]),
+    ("attention dropout group", [("{(uint32_t)j >> 3, (uint32_t)i", "{(uint32_t)j >> 2, (uint32_t)i", 0)]),
     ("dropout backward: value grad unmasked", [("double pv = p[j] * z;",
                                                 "double pv = p[j];", 0)]),
     ("P.V weights relative to the exact max", [("const double M = ceil(tmax);",
@@ -144,11 +147,17 @@ def _pins(lib):
         if oracle.philox4x32_10(ctr, key, lib=lib) != want:
             failed.append("philox kat")
             break
-    thr = oracle.dropout_threshold(0.5, lib=lib)
-    for (i, j) in ((3, 5), (7, 0), (9, 14)):
-        w = oracle.philox4x32_10([j >> 2, i, 1 * 4 + 2, 1], [77, 0], lib=lib)[j & 3]
-        if oracle.dropout_keep_attn(1, 2, 4, i, j, 0.5, 77, lib=lib) != (w >= thr):
+    thr, thr16 = oracle.dropout_threshold(0.5, lib=lib), oracle.dropout_threshold16(0.5, lib=lib)
+    for (i, j) in ((3, 5), (7, 0), (9, 14), (2, 10), (4, 3), (8, 22)):
+        w = oracle.philox4x32_10([j >> 3, i, 1 * 4 + 2, 1], [77, 0], lib=lib)
+        u = (w[(j & 7) >> 1] >> (16 * (j & 1))) & 0xFFFF
+        if oracle.dropout_keep_attn(1, 2, 4, i, j, 0.5, 77, lib=lib) != (u >= thr16):
             failed.append("dropout mapping")
+            break
+    for (m, n) in ((3, 5), (7, 0), (9, 14), (2, 10), (4, 3), (8, 22)):
+        w = oracle.philox4x32_10([n >> 2, m, 0, 2], [77, 0], lib=lib)[n & 3]
+        if oracle.dropout_keep_resid(m, n, 0.5, 77, lib=lib) != (w >= thr):
+            failed.append("residual dropout mapping")
             break
     pd, sd = 0.5, 77
     di = make_inputs(1, 5, 8, 2, dtype="f32", seed=11, w_std=0.4, proj_std=0.4,
