@@ -301,25 +301,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd2_bf16_kernel(
     rs = pair_sum32(rs);
     l += rs;
     if constexpr (DROP) {
-      // keys j0 + kt*32 + 8g + 4hi + e (e = 0..3) of query myq: one Philox
-      // call covers the 4 consecutive keys of register group g.  wq: this
-      // lane's keep bits (bit 16kt + 4g + e).
+      // keys j0 + kt*32 + 8g + 4hi + e (e = 0..3) of query myq.  The eight
+      // keys j0 + kt*32 + 8g + (0..7) share one Philox call whose 16-bit
+      // halves are their draws: lanes l and l + 32 (same query) split the
+      // two calls of group g (lane hi draws kt = hi), each keeps the two
+      // words of its own four keys and hands the other two to its partner
+      // with v_permlane32_swap (r[0] = x[l % 32], r[1] = x[l % 32 + 32]).
+      // wq: this lane's keep bits (bit 16kt + 4g + e).
       uint32_t wq = 0;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t jc = (uint32_t)(j0 + hi * 32 + 8 * g) >> 3;
+        const uint4 c = philox4x32_10(make_uint4(jc, (uint32_t)myq, (uint32_t)bh, 1u), drop.k0,
+                                      drop.k1);
+        const uint32_t own0 = hi ? c.z : c.x, own1 = hi ? c.w : c.y;
+        const uint32_t sx = hi ? c.x : c.z, sy = hi ? c.y : c.w;
+        const auto rx = __builtin_amdgcn_permlane32_swap(sx, sx, false, false);
+        const auto ry = __builtin_amdgcn_permlane32_swap(sy, sy, false, false);
+        const uint32_t got0 = hi ? rx[0] : rx[1], got1 = hi ? ry[0] : ry[1];
+        // words of kt = 0 and kt = 1 for this lane's four keys
+        const uint32_t wd[2][2] = {{hi ? got0 : own0, hi ? got1 : own1},
+                                   {hi ? own0 : got0, hi ? own1 : got1}};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint32_t jb = (uint32_t)(j0 + kt * 32 + 8 * g + 4 * hi);
-          const uint4 w = philox4x32_10(make_uint4(jb >> 2, (uint32_t)myq, (uint32_t)bh, 1u),
-                                        drop.k0, drop.k1);
-          const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const bool kp = wd[e] >= drop.thresh;
+            const uint32_t u = (wd[kt][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const bool kp = u >= drop.thresh16;
             if (!kp) sc[kt][4 * g + e] = 0.f;
             wq |= (uint32_t)kp << (16 * kt + 4 * g + e);
           }
-        }
+      }
       if (store_keep) {
         // lane o: keep bits of key j0 + o over the wave's 32 queries
         const uint32_t xk = keep_transpose(wq);

@@ -174,6 +174,8 @@ inline gpt_attn::DropParams make_drop(float p, unsigned long long seed) {
   d.k0 = (uint32_t)seed;
   d.k1 = (uint32_t)(seed >> 32);
   d.thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  const double t16 = floor((double)p * 65536.0);
+  d.thresh16 = t16 >= 65535.0 ? 0xFFFFu : (uint32_t)t16;
   d.scale = (float)(1.0 / (1.0 - (double)p));
   return d;
 }

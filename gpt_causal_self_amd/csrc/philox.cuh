@@ -9,11 +9,11 @@
 // advances by two Weyl constants between rounds.
 //
 // Dropout (nn.Dropout after the softmax and after c_proj; page "nanoGPT
-// architecture explained step by step", section 3): an element is dropped
-// iff its word of Philox(counter, key = seed) is below t = floor(p * 2^32);
-// kept elements are scaled by 1 / (1 - p).  Attention weight (b, h, i, j):
-// counter (j / 4, i, b * H + h, 1), word j % 4.  c_proj output (m, n):
-// counter (n / 4, m, 0, 2), word n % 4.
+// architecture explained step by step", section 3): kept elements are scaled
+// by 1 / (1 - p).  Attention weight (b, h, i, j): counter (j / 8, i, b * H + h,
+// 1), 16-bit half j % 2 of word (j % 8) / 2, dropped iff that half is below
+// floor(p * 2^16) (one call covers eight keys).  c_proj output (m, n):
+// counter (n / 4, m, 0, 2), word n % 4, dropped iff below floor(p * 2^32).
 #pragma once
 
 #include <stdint.h>
@@ -24,7 +24,8 @@ namespace gpt_attn {
 
 struct DropParams {
   uint32_t k0, k1;   // key: seed low / high word
-  uint32_t thresh;   // drop iff word < thresh
+  uint32_t thresh;   // c_proj output: drop iff word < thresh
+  uint32_t thresh16; // attention weights: drop iff 16-bit half < thresh16
   float scale;       // 1 / (1 - p)
 };
 

@@ -120,10 +120,12 @@ int gpt_attn_backward(gpt_attn_t h, const void *x, const void *W_attn,
  * section 3, attn_dropout and resid_dropout).  p = 0 (the default) is the
  * identity.  Masks come from the Philox4x32-10 counter-based generator
  * (Salmon et al., SC 2011) keyed by seed (low word, high word): attention
- * weight (b, h, query i, key j) uses counter (j/4, i, b*n_head + h, 1) and
- * output word j%4; c_proj output (row m = b*T + t, column n) uses counter
- * (n/4, m, 0, 2) and word n%4; an element is dropped iff its word is below
- * floor(p * 2^32), kept elements are scaled by 1/(1-p).  The softmax row is
+ * weight (b, h, query i, key j) uses counter (j/8, i, b*n_head + h, 1) and
+ * the 16-bit half j%2 (0: low) of output word (j%8)/2, dropped iff that half
+ * is below floor(p * 2^16) (capped at 2^16 - 1); c_proj output (row
+ * m = b*T + t, column n) uses counter (n/4, m, 0, 2) and word n%4, dropped
+ * iff that word is below floor(p * 2^32); kept elements are scaled by
+ * 1/(1-p).  The softmax row is
  * normalised over all visible keys before dropping.  A forward with
  * save_for_backward records p and seed, and gpt_attn_backward then returns
  * the exact gradient through the same masks (the upstream gradient of the

@@ -6,7 +6,9 @@ threshold on both sides, so the masks agree exactly; what remains is the
 rounding of the bf16 path, judged with the oracle that rounds q/k/v and the
 merged heads like the GPU (one ulp of the output plus 2^-8 of the row's
 largest output).  Dropped c_proj outputs are exactly zero on both sides,
-which checks the output mask bit for bit."""
+which checks the output mask bit for bit (a kept output can also be zero on
+the GPU, where its fp32 accumulator cancels the bias exactly: those few sit
+inside the rounding gate)."""
 from __future__ import annotations
 
 import numpy as np
@@ -53,7 +55,14 @@ def _check(g, r, what):
                              f"got {g[idx]!r} want {r[idx]!r} (bound {bound[idx]:.3e})")
     rel = np.linalg.norm(g - r) / np.linalg.norm(r)
     assert rel < 4e-3, f"{what}: normwise error {rel:.3e}"
-    assert np.array_equal(g == 0.0, r == 0.0), f"{what}: dropped outputs differ"
+    # every output the oracle drops is exactly zero on the GPU
+    dropped = r == 0.0
+    assert np.all(g[dropped] == 0.0), f"{what}: {(g[dropped] != 0.0).sum()} dropped outputs kept"
+    # a kept output is exactly zero on the GPU only where its fp32 accumulator
+    # cancels the bias exactly; the gate above admits that only within rounding
+    # of zero, and it is rare (about one output in 10^7 at the 124M shape)
+    extra = int(((g == 0.0) & ~dropped).sum())
+    assert extra <= max(2, g.size // 1_000_000), f"{what}: {extra} kept outputs are zero"
 
 
 @pytest.mark.parametrize("B,T,C,H,p,seed", [(2, 70, 256, 4, 0.1, 1), (3, 129, 128, 4, 0.5, 2),
