@@ -271,17 +271,21 @@ struct Epi2QKV {
 // t = 1 / (1 + p a), |e(a)| <= 1.5e-7.  With a = |v| / sqrt(2),
 // g(v) = v - v/2 erfc(a) for v >= 0 and v/2 erfc(a) for v < 0, so the negative
 // tail is a product (no cancellation in 1 + erf); |g - exact| <= |v| 7.5e-8
-// before rounding, far below the bf16 step of the stored activation.
+// before rounding, far below the bf16 step of the stored activation.  Both
+// signs in one form: g(v) = max(v, 0) - |v|/2 erfc(a).  The constants absorb
+// the scalings: with s = sqrt(log2 e) and a' = s a, exp(-a^2) = 2^(-a'^2),
+// t = 1 / (1 + (p / s) a'), and the five coefficients carry the 1/2, so a
+// value costs 13 VALU operations besides its rcp and exp2.
 __device__ __forceinline__ float gelu_erf(float v) {
-  const float a = fabsf(v) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, a, 1.f));
-  float q = fmaf(1.061405429f, t, -1.453152027f);
-  q = fmaf(q, t, 1.421413741f);
-  q = fmaf(q, t, -0.284496736f);
-  q = fmaf(q, t, 0.254829592f);
-  const float erfc = q * t * __builtin_amdgcn_exp2f(-a * a * 1.4426950408889634f);
-  const float h = 0.5f * v * erfc;
-  return v >= 0.f ? v - h : h;
+  constexpr double kS = 1.2011224087864498;  // sqrt(log2 e)
+  const float ap = fabsf(v) * (float)(0.70710678118654752 * kS);
+  const float t = __builtin_amdgcn_rcpf(fmaf((float)(0.3275911 / kS), ap, 1.f));
+  float q = fmaf((float)(0.5 * 1.061405429), t, (float)(0.5 * -1.453152027));
+  q = fmaf(q, t, (float)(0.5 * 1.421413741));
+  q = fmaf(q, t, (float)(0.5 * -0.284496736));
+  q = fmaf(q, t, (float)(0.5 * 0.254829592));
+  const float half_erfc = q * t * __builtin_amdgcn_exp2f(-(ap * ap));
+  return fmaf(-fabsf(v), half_erfc, fmaxf(v, 0.f));
 }
 
 // MLP c_fc epilogue: bias, exact GELU, rounding; row-major [M][ldc].
