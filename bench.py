@@ -448,6 +448,62 @@ def pmc_run_all(steps):
     print(f"pmc run: {steps} forward, {steps} training and {steps} MLP steps", flush=True)
 
 
+def _read_sclk(path):
+    """Current shader clock in MHz from an amdgpu pp_dpm_sclk file (the line
+    marked with '*' is the level in use; its value is the measured clock)."""
+    import re
+    with open(path) as f:
+        for line in f:
+            if line.rstrip().endswith("*"):
+                m = re.search(r"(\d+)\s*mhz", line, re.IGNORECASE)
+                return int(m.group(1)) if m else None
+    return None
+
+
+def sample_sclk(step, seconds=0.5, period=0.005):
+    """Shader clock while the workload runs: a thread reads the driver's
+    pp_dpm_sclk every `period` s while the caller's thread keeps issuing
+    step(i) for `seconds` (outside the timed regions).  Needs exactly one
+    amdgpu card in sysfs (else the clock cannot be tied to the device)."""
+    import glob
+    import statistics
+    import threading
+    import torch
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if len(files) != 1:
+        return {"error": f"{len(files)} pp_dpm_sclk files; cannot tell which is this device"}
+    path, vals, stop = files[0], [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                v = _read_sclk(path)
+            except OSError:
+                v = None
+            if v:
+                vals.append(v)
+            time.sleep(period)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    for i in range(20):
+        step(i)
+    th.start()
+    t0, i = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        step(i)
+        i += 1
+        if i % 200 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not vals:
+        return {"error": "no readable samples", "source": path}
+    return {"median": statistics.median(vals), "min": min(vals), "max": max(vals),
+            "samples": len(vals), "source": path,
+            "window": f"{i} forward steps over {seconds} s after the timed regions"}
+
+
 def time_calls(fn, n, warm=3):
     """Mean milliseconds per call of fn (launches on the current stream),
     from torch events around n back-to-back calls."""
@@ -743,6 +799,10 @@ def main():
            "event_layer_ms": round(mean["layer"], 5),
            "ms_per_step_with_stage_events": round(wall_events * 1e3 / args.steps, 5),
            "kernels": kernels, "roofline": roofline}
+    try:
+        out["sclk_mhz"] = sample_sclk(step)
+    except Exception as e:  # the clock is context; its absence is no failure
+        out["sclk_mhz"] = {"error": str(e)}
 
     if not args.no_train:
         try:
