@@ -26,9 +26,15 @@ __device__ __forceinline__ float bf2f(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// Two fp32 -> packed pair of bf16 (low half = a).
+// Two fp32 -> packed pair of bf16 (low half = a), round to nearest even as
+// f2bf.  Written as one two-lane vector conversion, which is a single
+// v_cvt_pk_bf16_f32 (two scalar conversions cost that instruction twice plus
+// a shift and an or).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  typedef float float2_v __attribute__((ext_vector_type(2)));
+  const bf16x2_v v = __builtin_convertvector((float2_v){a, b}, bf16x2_v);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // 32x32x16 bf16 MFMA, fp32 accumulate.  Lane l supplies A[l%32][k-slice of
