@@ -30,6 +30,15 @@ __device__ __forceinline__ float bf2f(bf16_t b) {
 // f2bf.  Written as one two-lane vector conversion, which is a single
 // v_cvt_pk_bf16_f32 (two scalar conversions cost that instruction twice plus
 // a shift and an or).
+// Non-temporal 16-byte store, for a call's final outputs (no later kernel of
+// the call reads them): the line goes out without staying dirty in the
+// XCD's L2, where the next kernel's traffic would otherwise write it back.
+__device__ __forceinline__ void store16_stream(void* p, uint4 w) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {w.x, w.y, w.z, w.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
   typedef float float2_v __attribute__((ext_vector_type(2)));

@@ -218,11 +218,12 @@ struct Epi2RowMajor {
     w.y = pack_bf16x2(v[2] + b[2], v[3] + b[3]);
     *reinterpret_cast<uint2*>(out + (size_t)m * ldc + n) = w;
   }
-  // staged path: bias is added before rounding into the LDS tile
+  // staged path: bias is added before rounding into the LDS tile; the
+  // output (y, dx) is a final one, stored non-temporally
   static constexpr bool kStaged = true;
   __device__ __forceinline__ const bf16_t* bias_ptr() const { return bias; }
   __device__ __forceinline__ void store8(int m, int n, uint4 w) const {
-    *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = w;
+    store16_stream(out + (size_t)m * ldc + n, w);
   }
 };
 

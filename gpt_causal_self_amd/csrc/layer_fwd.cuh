@@ -52,7 +52,7 @@ struct Epi2RowMajorRes {
     o.y = pack_bf16x2(v[2] + x[2], v[3] + x[3]);
     o.z = pack_bf16x2(v[4] + x[4], v[5] + x[5]);
     o.w = pack_bf16x2(v[6] + x[6], v[7] + x[7]);
-    *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = o;
+    store16_stream(out + (size_t)m * ldc + n, o);
   }
   __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
     float b[4] = {0.f, 0.f, 0.f, 0.f};
@@ -106,7 +106,7 @@ struct Epi2RowMajorDrop {
     float x[8];
     bf16x8_to_f32(rr, x);
     const uint2 lo = apply4(m, n, v, x), hi = apply4(m, n + 4, v + 4, x + 4);
-    *reinterpret_cast<uint4*>(out + (size_t)m * ldc + n) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    store16_stream(out + (size_t)m * ldc + n, make_uint4(lo.x, lo.y, hi.x, hi.y));
   }
   __device__ __forceinline__ void operator()(int m, int n, const float* v) const {
     float a[4] = {v[0], v[1], v[2], v[3]};
