@@ -39,6 +39,17 @@ __device__ __forceinline__ void store16_stream(void* p, uint4 w) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
+// 16-byte store written through the XCD's L2 (a buffer store with the sc1
+// cache policy), for a tensor that the next kernel reads, largely from other
+// XCDs: the line does not stay dirty in this XCD's L2, so no write-back of
+// it lands in the next kernel.  base: the tensor; off: byte offset, < 2^31.
+__device__ __forceinline__ void store16_wt(void* base, uint32_t off, uint4 w) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = {w.x, w.y, w.z, w.w};
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16 /* sc1 */);
+}
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
   typedef float float2_v __attribute__((ext_vector_type(2)));

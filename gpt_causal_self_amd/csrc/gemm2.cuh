@@ -236,6 +236,7 @@ struct Epi2QKV {
   bf16_t* qkv;
   const bf16_t* bias;  // [3C] or NULL
   int B, T, C, H, hs;
+  int wt;  // staged stores written through L2 (the tensor spans < 2^31 bytes)
   static constexpr bool kSplitOffsets = true;
   __device__ __forceinline__ size_t row_off(int m) const {  // (b, t) part
     const int bb = m / T, t = m - bb * T;
@@ -261,7 +262,11 @@ struct Epi2QKV {
   static constexpr bool kStaged = true;
   __device__ __forceinline__ const bf16_t* bias_ptr() const { return bias; }
   __device__ __forceinline__ void store8(int m, int n, uint4 w) const {
-    *reinterpret_cast<uint4*>(qkv + row_off(m) + col_off(n)) = w;
+    const size_t off = row_off(m) + col_off(n);
+    if (wt)
+      store16_wt(qkv, (uint32_t)(off * 2), w);
+    else
+      *reinterpret_cast<uint4*>(qkv + off) = w;
   }
 };
 

@@ -249,7 +249,7 @@ inline void layer_forward_bf16(const gpt_attn_handle* h, const bf16_t* x, int B,
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hs));
   bf16_t* qkv = (bf16_t*)h->qkv;
   bf16_t* o = (bf16_t*)h->o;
-  Epi2QKV e1{qkv, b_attn, B, T, C, H, hs};
+  Epi2QKV e1{qkv, b_attn, B, T, C, H, hs, 3 * head_elems * 2 < (size_t)1 << 31};
   mark(h, 0, st);
   launch_proj<GA_QKV_TILE, true, false, GA_QKV_OCC>(h, x, C, W_attn, 3 * C, M, 3 * C, C, e1, st);
   mark(h, 1, st);
