@@ -26,10 +26,6 @@ __device__ __forceinline__ float bf2f(bf16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
 }
 
-// Two fp32 -> packed pair of bf16 (low half = a), round to nearest even as
-// f2bf.  Written as one two-lane vector conversion, which is a single
-// v_cvt_pk_bf16_f32 (two scalar conversions cost that instruction twice plus
-// a shift and an or).
 // Non-temporal 16-byte store, for a call's final outputs (no later kernel of
 // the call reads them): the line goes out without staying dirty in the
 // XCD's L2, where the next kernel's traffic would otherwise write it back.
@@ -50,6 +46,11 @@ __device__ __forceinline__ void store16_wt(void* base, uint32_t off, uint4 w) {
       __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7fffffff, 0x00020000);
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 16 /* sc1 */);
 }
+
+// Two fp32 -> packed pair of bf16 (low half = a), round to nearest even as
+// f2bf.  Written as one two-lane vector conversion, which is a single
+// v_cvt_pk_bf16_f32 (two scalar conversions cost that instruction twice plus
+// a shift and an or).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
   typedef float float2_v __attribute__((ext_vector_type(2)));
